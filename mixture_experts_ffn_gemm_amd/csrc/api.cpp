@@ -1,0 +1,361 @@
+// C-ABI entry points of the MI355X DeepSeekMoE layer forward: argument
+// validation (pure host code, before any launch), workspace layout, and the
+// orchestration of the gfx950 kernels on the caller's streams.
+#include <cmath>
+#include <cstdio>
+#include <string>
+
+#include "../../include/moe.h"
+#include "moe_internal.h"
+
+using namespace moe;
+
+namespace {
+
+thread_local std::string g_err;
+
+int fail(int status, const std::string& msg) {
+  g_err = msg;
+  return status;
+}
+
+#define MOE_HIP_CHECK(expr)                                                      \
+  do {                                                                           \
+    hipError_t e_ = (expr);                                                      \
+    if (e_ != hipSuccess)                                                        \
+      return fail(MOE_ERR_HIP, std::string(#expr) + ": " + hipGetErrorString(e_)); \
+  } while (0)
+
+size_t act_bytes(int dt) { return dt == MOE_F32 ? 4 : 2; }
+size_t align_up(size_t v) { return (v + 255) & ~size_t(255); }
+
+struct Layout {
+  size_t z, wr3, idx, gate, hist, base, rank, counts, offsets, row_token, slot_row, h, y, hs, ys,
+      shoff, total;
+  int64_t h_elems;  // capacity of the h region in activation elements
+};
+
+Layout make_layout(const moe_config& c) {
+  Layout L{};
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t o = off;
+    off += align_up(bytes);
+    return o;
+  };
+  const int64_t T = c.T, N = c.n_routed, d = c.d, I = c.inter, S = c.n_shared;
+  const int64_t slots = T * c.k;
+  const int64_t nchunks = cdiv(slots, kPermChunk);
+  const size_t as = act_bytes(c.act_dtype);
+  L.z = take(T * N * 4);
+  L.wr3 = take(N * 3 * d * 2);
+  L.idx = take(slots * 4);
+  L.gate = take(slots * 4);
+  L.hist = take(nchunks * N * 4);
+  L.base = take(nchunks * N * 4);
+  L.rank = take(slots * 4);
+  L.counts = take(N * 4);
+  L.offsets = take((N + 1) * 4);
+  L.row_token = take(slots * 4);
+  L.slot_row = take(slots * 4);
+  const int64_t rows_max = slots > T ? slots : T;
+  const int64_t inter_max = S * I > I ? S * I : I;
+  L.h_elems = rows_max * inter_max;
+  L.h = take(L.h_elems * as);
+  L.y = take(slots * d * as);
+  L.hs = take(T * S * I * as);
+  L.ys = take(S > 0 ? T * d * as : 0);
+  L.shoff = take(2 * 4);
+  L.total = off;
+  return L;
+}
+
+int check_config(const moe_config* c) {
+  if (!c) return fail(MOE_ERR_INVALID_ARG, "cfg is NULL");
+  if (c->T < 0) return fail(MOE_ERR_INVALID_ARG, "T must be >= 0");
+  if (c->d <= 0 || c->inter <= 0) return fail(MOE_ERR_INVALID_ARG, "d and inter must be > 0");
+  if (c->n_routed < 1 || c->n_routed > 256)
+    return fail(MOE_ERR_UNSUPPORTED, "n_routed must be in [1, 256]");
+  if (c->k < 1 || c->k > c->n_routed) return fail(MOE_ERR_INVALID_ARG, "k must be in [1, n_routed]");
+  if (c->k > 64) return fail(MOE_ERR_UNSUPPORTED, "k must be <= 64");
+  if (c->n_groups < 1 || c->n_groups > 64 || c->n_routed % c->n_groups != 0)
+    return fail(MOE_ERR_INVALID_ARG, "n_groups must be in [1, 64] and divide n_routed");
+  if (c->topk_groups < 1 || c->topk_groups > c->n_groups)
+    return fail(MOE_ERR_INVALID_ARG, "topk_groups must be in [1, n_groups]");
+  const int gs = c->n_routed / c->n_groups;
+  if (c->n_groups > 1 && (c->group_topn < 1 || c->group_topn > gs))
+    return fail(MOE_ERR_INVALID_ARG, "group_topn must be in [1, n_routed / n_groups]");
+  if ((int64_t)c->k > (int64_t)c->topk_groups * gs)
+    return fail(MOE_ERR_INVALID_ARG, "k exceeds the experts of the kept groups");
+  if (c->gate != MOE_GATE_SOFTMAX && c->gate != MOE_GATE_SIGMOID_NORM)
+    return fail(MOE_ERR_INVALID_ARG, "unknown gate mode");
+  if (!std::isfinite(c->route_scale)) return fail(MOE_ERR_INVALID_ARG, "route_scale not finite");
+  if (c->n_shared < 0) return fail(MOE_ERR_INVALID_ARG, "n_shared must be >= 0");
+  if (c->out_dtype != MOE_F32 && c->out_dtype != MOE_BF16)
+    return fail(MOE_ERR_UNSUPPORTED, "out_dtype must be F32 or BF16");
+  const bool f32 = c->act_dtype == MOE_F32 && c->w_dtype == MOE_F32 && c->w_block == 0;
+  const bool bf16 = c->act_dtype == MOE_BF16 && c->w_dtype == MOE_BF16 && c->w_block == 0;
+  const bool fp8 = c->act_dtype == MOE_BF16 && c->w_dtype == MOE_FP8_E4M3 && c->w_block == 128;
+  if (!(f32 || bf16 || fp8))
+    return fail(MOE_ERR_UNSUPPORTED,
+                "supported (act, w, w_block): (F32, F32, 0), (BF16, BF16, 0), (BF16, FP8_E4M3, 128)");
+  const int q = f32 ? 64 : 128;
+  if (c->d % q != 0 || c->inter % q != 0)
+    return fail(MOE_ERR_UNSUPPORTED, f32 ? "f32 path needs d % 64 == 0 and inter % 64 == 0"
+                                         : "bf16/fp8 paths need d % 128 == 0 and inter % 128 == 0");
+  if (c->T * (int64_t)c->k > 0x7fffffffLL) return fail(MOE_ERR_UNSUPPORTED, "T * k must fit int32");
+  return MOE_OK;
+}
+
+int check_ws(const moe_config* c, void* ws, size_t ws_bytes) {
+  const size_t need = make_layout(*c).total;
+  if (!ws || ws_bytes < need)
+    return fail(MOE_ERR_WORKSPACE, "workspace of " + std::to_string(need) + " bytes required, got " +
+                                       std::to_string(ws ? ws_bytes : 0));
+  return MOE_OK;
+}
+
+template <typename P>
+P* at(void* ws, size_t off) {
+  return (P*)((char*)ws + off);
+}
+
+int run_router(const moe_config* c, const void* x, const float* W_r, const float* b,
+               int32_t* idx, float* gate, float* scores, void* ws, hipStream_t s) {
+  const Layout L = make_layout(*c);
+  float* z = at<float>(ws, L.z);
+  MOE_HIP_CHECK(launch_router_logits_simt(c->act_dtype == MOE_BF16, x, W_r, z, c->T, c->d,
+                                          c->n_routed, s));
+  MOE_HIP_CHECK(launch_router_select(z, b, c->T, c->n_routed, c->k, c->n_groups, c->topk_groups,
+                                     c->group_topn, c->gate, c->route_scale, idx, gate, scores, s));
+  return MOE_OK;
+}
+
+int run_expert_ffn(const moe_config* c, int n_experts, const int32_t* offsets, int64_t max_rows,
+                   int inter, const void* x_rows, const int32_t* row_index, const void* W1,
+                   const void* W3, const void* W2, const float* s1, const float* s3,
+                   const float* s2, void* h, void* y_rows, hipStream_t s) {
+  GroupedGemmArgs up{};
+  up.A = x_rows;
+  up.row_index = row_index;
+  up.offsets = offsets;
+  up.n_groups = n_experts;
+  up.max_rows = max_rows;
+  up.B0 = W1;
+  up.B1 = W3;
+  up.S0 = s1;
+  up.S1 = s3;
+  up.C = h;
+  up.Nout = inter;
+  up.K = c->d;
+  GroupedGemmArgs dn{};
+  dn.A = h;
+  dn.row_index = nullptr;
+  dn.offsets = offsets;
+  dn.n_groups = n_experts;
+  dn.max_rows = max_rows;
+  dn.B0 = W2;
+  dn.B1 = nullptr;
+  dn.S0 = s2;
+  dn.S1 = nullptr;
+  dn.C = y_rows;
+  dn.Nout = c->d;
+  dn.K = inter;
+  if (c->w_dtype == MOE_F32) {
+    MOE_HIP_CHECK(launch_gemm_f32_swiglu(up, s));
+    MOE_HIP_CHECK(launch_gemm_f32_store(dn, s));
+  } else if (c->w_dtype == MOE_BF16) {
+    MOE_HIP_CHECK(launch_gemm_bf16_swiglu(up, s));
+    MOE_HIP_CHECK(launch_gemm_bf16_store(dn, s));
+  } else {
+    MOE_HIP_CHECK(launch_gemm_fp8_swiglu(up, s));
+    MOE_HIP_CHECK(launch_gemm_fp8_store(dn, s));
+  }
+  return MOE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* moe_status_string(int status) {
+  switch (status) {
+    case MOE_OK: return "MOE_OK";
+    case MOE_ERR_INVALID_ARG: return "MOE_ERR_INVALID_ARG";
+    case MOE_ERR_UNSUPPORTED: return "MOE_ERR_UNSUPPORTED";
+    case MOE_ERR_WORKSPACE: return "MOE_ERR_WORKSPACE";
+    case MOE_ERR_HIP: return "MOE_ERR_HIP";
+    default: return "MOE_UNKNOWN_STATUS";
+  }
+}
+
+const char* moe_last_error(void) { return g_err.c_str(); }
+
+const char* moe_version(void) { return "moe-mi355x 0.1 (gfx950)"; }
+
+size_t moe_workspace_size(const moe_config* cfg) {
+  if (check_config(cfg) != MOE_OK) return 0;
+  return make_layout(*cfg).total;
+}
+
+int moe_router(const moe_config* cfg, const void* x, const float* W_r, const float* b,
+               int32_t* topk_idx, float* topk_gate, float* scores, void* ws, size_t ws_bytes,
+               void* stream) {
+  g_err.clear();
+  int st = check_config(cfg);
+  if (st) return st;
+  if (cfg->T == 0) return MOE_OK;
+  if (!x || !W_r || !topk_idx || !topk_gate)
+    return fail(MOE_ERR_INVALID_ARG, "x, W_r, topk_idx and topk_gate must be non-NULL");
+  if ((st = check_ws(cfg, ws, ws_bytes))) return st;
+  return run_router(cfg, x, W_r, b, topk_idx, topk_gate, scores, ws, (hipStream_t)stream);
+}
+
+int moe_permute(const moe_config* cfg, const int32_t* topk_idx, const void* x, int32_t* counts,
+                int32_t* offsets, int32_t* row_token, int32_t* slot_row, void* x_perm, void* ws,
+                size_t ws_bytes, void* stream) {
+  g_err.clear();
+  int st = check_config(cfg);
+  if (st) return st;
+  if (!counts || !offsets) return fail(MOE_ERR_INVALID_ARG, "counts and offsets must be non-NULL");
+  if (cfg->T > 0 && (!topk_idx || !row_token || !slot_row))
+    return fail(MOE_ERR_INVALID_ARG, "topk_idx, row_token and slot_row must be non-NULL");
+  if (x_perm && !x) return fail(MOE_ERR_INVALID_ARG, "x_perm needs x");
+  if ((st = check_ws(cfg, ws, ws_bytes))) return st;
+  hipStream_t s = (hipStream_t)stream;
+  const Layout L = make_layout(*cfg);
+  if (cfg->T == 0) {
+    MOE_HIP_CHECK(launch_fill_i32(counts, cfg->n_routed, 0, s));
+    MOE_HIP_CHECK(launch_fill_i32(offsets, cfg->n_routed + 1, 0, s));
+    return MOE_OK;
+  }
+  MOE_HIP_CHECK(launch_permute(topk_idx, cfg->T, cfg->k, cfg->n_routed, at<int32_t>(ws, L.hist),
+                               at<int32_t>(ws, L.base), at<int32_t>(ws, L.rank), counts, offsets,
+                               row_token, slot_row, s));
+  if (x_perm)
+    MOE_HIP_CHECK(launch_gather_rows(x, row_token, x_perm, cfg->T * cfg->k,
+                                     (int64_t)cfg->d * act_bytes(cfg->act_dtype), s));
+  return MOE_OK;
+}
+
+int moe_expert_ffn(const moe_config* cfg, int32_t n_experts, const int32_t* offsets,
+                   int64_t max_rows, int32_t inter_override, const void* x_rows,
+                   const int32_t* row_index, const void* W1, const void* W3, const void* W2,
+                   const float* s1, const float* s3, const float* s2, void* y_rows, void* ws,
+                   size_t ws_bytes, void* stream) {
+  g_err.clear();
+  int st = check_config(cfg);
+  if (st) return st;
+  if (n_experts < 1 || n_experts > 256)
+    return fail(MOE_ERR_INVALID_ARG, "n_experts must be in [1, 256]");
+  if (max_rows < 0) return fail(MOE_ERR_INVALID_ARG, "max_rows must be >= 0");
+  if (max_rows == 0) return MOE_OK;
+  if (!offsets || !x_rows || !W1 || !W3 || !W2 || !y_rows)
+    return fail(MOE_ERR_INVALID_ARG, "offsets, x_rows, W1, W3, W2 and y_rows must be non-NULL");
+  const bool fp8 = cfg->w_dtype == MOE_FP8_E4M3;
+  if (fp8 && (!s1 || !s3 || !s2)) return fail(MOE_ERR_INVALID_ARG, "fp8 weights need s1, s3, s2");
+  if (!fp8 && (s1 || s3 || s2)) return fail(MOE_ERR_INVALID_ARG, "scales given for non-fp8 weights");
+  const int inter = inter_override > 0 ? inter_override : cfg->inter;
+  const int q = cfg->w_dtype == MOE_F32 ? 64 : 128;
+  if (inter % q != 0) return fail(MOE_ERR_UNSUPPORTED, "inter_override must be a multiple of 64/128");
+  if ((st = check_ws(cfg, ws, ws_bytes))) return st;
+  const Layout L = make_layout(*cfg);
+  if (max_rows * (int64_t)inter > L.h_elems)
+    return fail(MOE_ERR_WORKSPACE, "max_rows * inter exceeds the workspace sized for this config");
+  if (max_rows > 0x7fffffffLL) return fail(MOE_ERR_UNSUPPORTED, "max_rows must fit int32");
+  return run_expert_ffn(cfg, n_experts, offsets, max_rows, inter, x_rows, row_index, W1, W3, W2,
+                        s1, s3, s2, at<void>(ws, L.h), y_rows, (hipStream_t)stream);
+}
+
+int moe_combine(const moe_config* cfg, const void* y_perm, const int32_t* slot_row,
+                const float* topk_gate, const void* y_shared, const void* residual, void* out,
+                void* stream) {
+  g_err.clear();
+  int st = check_config(cfg);
+  if (st) return st;
+  if (cfg->T == 0) return MOE_OK;
+  if (!y_perm || !slot_row || !topk_gate || !out)
+    return fail(MOE_ERR_INVALID_ARG, "y_perm, slot_row, topk_gate and out must be non-NULL");
+  MOE_HIP_CHECK(launch_combine(cfg->act_dtype == MOE_BF16, cfg->out_dtype == MOE_BF16, y_perm,
+                               slot_row, topk_gate, y_shared, residual, out, cfg->T, cfg->d,
+                               cfg->k, (hipStream_t)stream));
+  return MOE_OK;
+}
+
+int moe_forward(const moe_config* cfg, const void* x, const float* W_r, const float* b,
+                const void* W1, const void* W3, const void* W2, const float* s1, const float* s3,
+                const float* s2, const void* W1s, const void* W3s, const void* W2s,
+                const float* s1s, const float* s3s, const float* s2s, void* out,
+                int32_t* topk_idx_out, float* topk_gate_out, int32_t* counts_out, void* ws,
+                size_t ws_bytes, void* stream_main, void* stream_side) {
+  g_err.clear();
+  int st = check_config(cfg);
+  if (st) return st;
+  const moe_config& c = *cfg;
+  if (c.T == 0) {
+    if (counts_out) MOE_HIP_CHECK(launch_fill_i32(counts_out, c.n_routed, 0, (hipStream_t)stream_main));
+    return MOE_OK;
+  }
+  if (!x || !W_r || !W1 || !W3 || !W2 || !out)
+    return fail(MOE_ERR_INVALID_ARG, "x, W_r, W1, W3, W2 and out must be non-NULL");
+  const bool fp8 = c.w_dtype == MOE_FP8_E4M3;
+  if (fp8 && (!s1 || !s3 || !s2)) return fail(MOE_ERR_INVALID_ARG, "fp8 weights need s1, s3, s2");
+  if (c.n_shared > 0) {
+    if (!W1s || !W3s || !W2s) return fail(MOE_ERR_INVALID_ARG, "shared weights must be non-NULL");
+    if (fp8 && (!s1s || !s3s || !s2s))
+      return fail(MOE_ERR_INVALID_ARG, "fp8 shared weights need s1s, s3s, s2s");
+  }
+  if ((st = check_ws(cfg, ws, ws_bytes))) return st;
+  const Layout L = make_layout(c);
+  hipStream_t sm = (hipStream_t)stream_main;
+  hipStream_t ss = stream_side ? (hipStream_t)stream_side : sm;
+  const bool two_streams = ss != sm && c.n_shared > 0;
+
+  struct Events {  // destroyed on every return path; pending events are released by HIP
+    hipEvent_t fork = nullptr, join = nullptr;
+    ~Events() {
+      if (fork) (void)hipEventDestroy(fork);
+      if (join) (void)hipEventDestroy(join);
+    }
+  } evs;
+  hipEvent_t& ev_fork = evs.fork;
+  hipEvent_t& ev_join = evs.join;
+  if (two_streams) {
+    MOE_HIP_CHECK(hipEventCreateWithFlags(&ev_fork, hipEventDisableTiming));
+    MOE_HIP_CHECK(hipEventCreateWithFlags(&ev_join, hipEventDisableTiming));
+    MOE_HIP_CHECK(hipEventRecord(ev_fork, sm));
+    MOE_HIP_CHECK(hipStreamWaitEvent(ss, ev_fork, 0));
+  }
+  void* ys = nullptr;
+  if (c.n_shared > 0) {
+    // shared MLP of width S * I over every token (one expert, rows {0, T})
+    int32_t* shoff = at<int32_t>(ws, L.shoff);
+    ys = at<void>(ws, L.ys);
+    MOE_HIP_CHECK(launch_set_range(shoff, (int32_t)c.T, ss));
+    st = run_expert_ffn(cfg, 1, shoff, c.T, c.n_shared * c.inter, x, nullptr, W1s, W3s, W2s, s1s,
+                        s3s, s2s, at<void>(ws, L.hs), ys, ss);
+    if (st) return st;
+    if (two_streams) MOE_HIP_CHECK(hipEventRecord(ev_join, ss));
+  }
+
+  int32_t* idx = topk_idx_out ? topk_idx_out : at<int32_t>(ws, L.idx);
+  float* gate = topk_gate_out ? topk_gate_out : at<float>(ws, L.gate);
+  int32_t* counts = counts_out ? counts_out : at<int32_t>(ws, L.counts);
+  int32_t* offsets = at<int32_t>(ws, L.offsets);
+  int32_t* row_token = at<int32_t>(ws, L.row_token);
+  int32_t* slot_row = at<int32_t>(ws, L.slot_row);
+  if ((st = run_router(cfg, x, W_r, b, idx, gate, nullptr, ws, sm))) return st;
+  MOE_HIP_CHECK(launch_permute(idx, c.T, c.k, c.n_routed, at<int32_t>(ws, L.hist),
+                               at<int32_t>(ws, L.base), at<int32_t>(ws, L.rank), counts, offsets,
+                               row_token, slot_row, sm));
+  void* y = at<void>(ws, L.y);
+  st = run_expert_ffn(cfg, c.n_routed, offsets, c.T * c.k, c.inter, x, row_token, W1, W3, W2, s1,
+                      s3, s2, at<void>(ws, L.h), y, sm);
+  if (st) return st;
+  if (two_streams) MOE_HIP_CHECK(hipStreamWaitEvent(sm, ev_join, 0));
+  MOE_HIP_CHECK(launch_combine(c.act_dtype == MOE_BF16, c.out_dtype == MOE_BF16, y, slot_row, gate,
+                               ys, x, out, c.T, c.d, c.k, sm));
+  return MOE_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,81 @@
+// Device-side tile scheduling for the grouped (per-expert) GEMMs.
+//
+// The launch is sized on the host from an upper bound of the row count
+// (max_rows / BM + n_groups M-tiles) and never waits for the real expert
+// counts: every workgroup rebuilds the per-expert tile prefix from the device
+// offsets in LDS, exits if its slot is past the real work, and otherwise maps
+// its slot to (expert, N-tile, M-tile).  Experts with no rows own no tile, so
+// their weights are never read.
+//
+// XCD-aware order: consecutive workgroup ids go round-robin over the 8 XCDs
+// (each with its own L2), so slot w runs tile xcd(w) * per + w / 8.  Each XCD
+// thereby walks one contiguous range of tiles, ordered expert-major, then
+// N-tile, then M-tile: the M-tiles that share a weight N-tile are resident on
+// the same XCD at the same time and read it through the same L2.
+#pragma once
+#include "moe_internal.h"
+#include "wave_utils.h"
+
+namespace moe {
+
+constexpr int kMaxGroups = 256;
+constexpr int kNumXcd = 8;
+
+struct TileCoord {
+  int group;
+  int64_t row0;  // first row of the tile
+  int64_t rend;  // end of the group's rows
+  int n0;        // first output column
+};
+
+// Must be called by all NT threads of the block.  Returns false when the
+// block has no tile (uniformly for the whole block).
+template <int NT>
+__device__ __forceinline__ bool grouped_tile_lookup(const int32_t* __restrict__ offsets,
+                                                    int n_groups, int BM, int BN, int Nout,
+                                                    int* s_ts /* kMaxGroups+1 */,
+                                                    int* s_scratch /* NT/64 */, int* s_info,
+                                                    TileCoord* tc) {
+  const int tid = threadIdx.x;
+  int tiles = 0;
+  if (tid < n_groups) {
+    const int cnt = offsets[tid + 1] - offsets[tid];
+    tiles = (cnt + BM - 1) / BM;
+  }
+  int total_m;
+  const int incl = block_incl_scan<NT>(tiles, s_scratch, &total_m);
+  if (tid < n_groups) s_ts[tid + 1] = incl;
+  if (tid == 0) s_ts[0] = 0;
+  const int n_tiles_n = Nout / BN;
+  const int total = total_m * n_tiles_n;
+  const int per = (total + kNumXcd - 1) / kNumXcd;
+  const int w = blockIdx.x;
+  const int j = w / kNumXcd, xcd = w % kNumXcd;
+  if (j >= per) return false;
+  const int L = xcd * per + j;
+  if (L >= total) return false;
+  __syncthreads();
+  if (tid < n_groups) {
+    const int lo = s_ts[tid] * n_tiles_n, hi = s_ts[tid + 1] * n_tiles_n;
+    if (L >= lo && L < hi) s_info[0] = tid;
+  }
+  __syncthreads();
+  const int g = s_info[0];
+  const int tiles_g = s_ts[g + 1] - s_ts[g];
+  const int rem = L - s_ts[g] * n_tiles_n;
+  const int nt = rem / tiles_g, mt = rem % tiles_g;
+  tc->group = g;
+  tc->row0 = (int64_t)offsets[g] + (int64_t)mt * BM;
+  tc->rend = offsets[g + 1];
+  tc->n0 = nt * BN;
+  return true;
+}
+
+// Upper bound of the number of workgroups a grouped launch needs.
+inline int64_t grouped_grid(int64_t max_rows, int n_groups, int BM, int BN, int Nout) {
+  const int64_t mt = max_rows / BM + n_groups;
+  const int64_t n = mt * (Nout / BN);
+  return ((n + kNumXcd - 1) / kNumXcd) * kNumXcd;
+}
+
+}  // namespace moe

@@ -1,0 +1,96 @@
+// Internal declarations shared by the gfx950 kernels and the C-ABI host code.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace moe {
+
+// ---------------------------------------------------------------- helpers
+typedef uint16_t bf16_t;  // bfloat16 bit pattern
+
+__device__ __forceinline__ float bf16_to_f32(uint16_t v) {
+  return __uint_as_float(((uint32_t)v) << 16);
+}
+// float -> bfloat16, round to nearest even (NaN stays NaN)
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x40u);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+
+template <typename T> struct ElemIO;
+template <> struct ElemIO<float> {
+  static __device__ __forceinline__ float load(const float* p) { return *p; }
+  static __device__ __forceinline__ void store(float* p, float v) { *p = v; }
+};
+template <> struct ElemIO<bf16_t> {
+  static __device__ __forceinline__ float load(const bf16_t* p) { return bf16_to_f32(*p); }
+  static __device__ __forceinline__ void store(bf16_t* p, float v) { *p = f32_to_bf16(v); }
+};
+
+__host__ __device__ inline int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+// ---------------------------------------------------------------- launchers
+// Every launcher enqueues on `stream` and returns hipGetLastError().
+
+// Router logits z[T, N] = x[T, d] . W_r[N, d]^T in fp32 (SIMT, fp32 FMA).
+hipError_t launch_router_logits_simt(bool x_bf16, const void* x, const float* W_r, float* z,
+                                     int64_t T, int d, int N, hipStream_t stream);
+
+// Router logits on MFMA: W_r split into three bf16 planes [N, 3d] (hi, mid, lo
+// residual parts whose sum is W_r exactly), x bf16.
+hipError_t launch_router_split_wr(const float* W_r, bf16_t* wr3, int d, int N, hipStream_t s);
+hipError_t launch_router_logits_mfma(const bf16_t* x, const bf16_t* wr3, float* z,
+                                     int64_t T, int d, int N, hipStream_t stream);
+
+// Scores, group-limited top-k and gates from z.
+hipError_t launch_router_select(const float* z, const float* b, int64_t T, int N, int k,
+                                int n_groups, int topk_groups, int group_topn, int gate,
+                                float route_scale, int32_t* idx, float* gates, float* scores,
+                                hipStream_t stream);
+
+// Counting-sort permutation of the S = T*k slots.
+constexpr int kPermChunk = 256;  // slots per wavefront chunk
+hipError_t launch_permute(const int32_t* idx, int64_t T, int k, int N, int32_t* hist,
+                          int32_t* base, int32_t* rank, int32_t* counts, int32_t* offsets,
+                          int32_t* row_token, int32_t* slot_row, hipStream_t stream);
+hipError_t launch_fill_i32(int32_t* p, int64_t n, int32_t value, hipStream_t stream);
+// p[0] = 0, p[1] = n: the row range of a single group covering n rows
+hipError_t launch_set_range(int32_t* p, int32_t n, hipStream_t stream);
+hipError_t launch_gather_rows(const void* x, const int32_t* row_token, void* x_perm,
+                              int64_t rows, int64_t row_bytes, hipStream_t stream);
+
+// Grouped GEMMs.  Group g owns rows [offsets[g], offsets[g+1]); its weight
+// matrix is B + g * Nout * K, stored [Nout, K].
+struct GroupedGemmArgs {
+  const void* A;            // activation rows [*, K]
+  const int32_t* row_index; // nullable gather map
+  const int32_t* offsets;   // [n_groups + 1] device
+  int n_groups;
+  int64_t max_rows;
+  const void* B0;           // [G, Nout, K]  (W1 or W2)
+  const void* B1;           // [G, Nout, K]  (W3) for the SwiGLU epilogue, else null
+  const float* S0;          // fp8 block scales [G, Nout/128, K/128] or null
+  const float* S1;
+  void* C;                  // [rows, Nout]
+  int Nout;
+  int K;
+};
+// bf16 MFMA (act bf16, w bf16)
+hipError_t launch_gemm_bf16_swiglu(const GroupedGemmArgs& a, hipStream_t s);
+hipError_t launch_gemm_bf16_store(const GroupedGemmArgs& a, hipStream_t s);
+// fp32 SIMT (act f32, w f32)
+hipError_t launch_gemm_f32_swiglu(const GroupedGemmArgs& a, hipStream_t s);
+hipError_t launch_gemm_f32_store(const GroupedGemmArgs& a, hipStream_t s);
+// fp8 block-scaled weights, bf16 activations, small row counts (decode)
+hipError_t launch_gemm_fp8_swiglu(const GroupedGemmArgs& a, hipStream_t s);
+hipError_t launch_gemm_fp8_store(const GroupedGemmArgs& a, hipStream_t s);
+
+// out = residual + y_shared + sum_j gate_j * y_perm[slot_row]
+hipError_t launch_combine(bool act_bf16, bool out_bf16, const void* y_perm,
+                          const int32_t* slot_row, const float* gate, const void* y_shared,
+                          const void* residual, void* out, int64_t T, int d, int k,
+                          hipStream_t stream);
+
+}  // namespace moe

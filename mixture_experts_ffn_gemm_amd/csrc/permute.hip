@@ -1,0 +1,157 @@
+// Counting-sort permutation of (token, expert) slots on gfx950.
+//
+// The reference forward shown on open-model-atlas ("DeepSeek-V3.2-Exp -
+// Mixture of experts", code excerpt of the MoE forward) counts the tokens of
+// every expert with a bincount, skips experts with none, and gathers each
+// expert's rows with a where/index pair.  Here the same grouping is one stable
+// counting sort on the device (no host round trip):
+//   1. hist:    one wavefront per chunk of 256 slots counts its experts in LDS
+//               and records each slot's rank among equal experts of the chunk
+//               (ballot + popcount, in slot order);
+//   2. scan:    one block per expert scans the chunk counts -> per-chunk base
+//               and the expert's total;
+//   3. scatter: row = offset[e] + base[chunk][e] + rank; row_token / slot_row.
+// Rows are ordered by expert, then by slot index f = t*k + j (stable).
+#include "moe_internal.h"
+#include "wave_utils.h"
+
+namespace moe {
+
+__global__ __launch_bounds__(256) void permute_hist_kernel(const int32_t* __restrict__ idx,
+                                                           int64_t S, int N, int nchunks,
+                                                           int32_t* __restrict__ hist,
+                                                           int32_t* __restrict__ rank) {
+  extern __shared__ int cnt_all[];  // 4 * N
+  const int w = threadIdx.x >> 6, lane = lane_id();
+  const int c = blockIdx.x * 4 + w;
+  int* cnt = cnt_all + w * N;
+  for (int i = lane; i < N; i += 64) cnt[i] = 0;
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+  __builtin_amdgcn_wave_barrier();
+  if (c >= nchunks) return;
+  const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+  for (int it = 0; it < kPermChunk / 64; ++it) {
+    const int64_t f = (int64_t)c * kPermChunk + it * 64 + lane;
+    const bool valid = f < S;
+    const int e = valid ? idx[f] : -1;
+    uint64_t todo = __ballot(valid);
+    int r = 0;
+    while (todo) {
+      const int leader = __ffsll((unsigned long long)todo) - 1;
+      const int le = __shfl(e, leader, 64);
+      const uint64_t m = __ballot(e == le);
+      const int base = cnt[le];
+      if (e == le) r = base + __popcll(m & lt_mask);
+      __builtin_amdgcn_wave_barrier();
+      if (lane == leader) cnt[le] = base + __popcll(m);
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+      __builtin_amdgcn_wave_barrier();
+      todo &= ~m;
+    }
+    if (valid) rank[f] = r;
+  }
+  for (int i = lane; i < N; i += 64) hist[(int64_t)c * N + i] = cnt[i];
+}
+
+__global__ __launch_bounds__(256) void permute_scan_kernel(const int32_t* __restrict__ hist,
+                                                           int nchunks, int N,
+                                                           int32_t* __restrict__ base,
+                                                           int32_t* __restrict__ counts) {
+  __shared__ int scratch[4];
+  const int e = blockIdx.x;
+  int carry = 0;
+  for (int c0 = 0; c0 < nchunks; c0 += 256) {
+    const int c = c0 + threadIdx.x;
+    const int v = c < nchunks ? hist[(int64_t)c * N + e] : 0;
+    int tot;
+    const int incl = block_incl_scan<256>(v, scratch, &tot);
+    if (c < nchunks) base[(int64_t)c * N + e] = carry + incl - v;
+    carry += tot;
+  }
+  if (threadIdx.x == 0) counts[e] = carry;
+}
+
+// One block per chunk of 256 slots; every block rebuilds the expert offsets
+// from counts (N <= 256) and block 0 publishes them.
+__global__ __launch_bounds__(256) void permute_scatter_kernel(
+    const int32_t* __restrict__ idx, int64_t S, int k, int N, const int32_t* __restrict__ counts,
+    const int32_t* __restrict__ base, const int32_t* __restrict__ rank,
+    int32_t* __restrict__ offsets, int32_t* __restrict__ row_token,
+    int32_t* __restrict__ slot_row) {
+  __shared__ int s_off[257];
+  __shared__ int scratch[4];
+  const int tid = threadIdx.x;
+  const int v = tid < N ? counts[tid] : 0;
+  int tot;
+  const int incl = block_incl_scan<256>(v, scratch, &tot);
+  if (tid < N) s_off[tid] = incl - v;
+  if (tid == 0) s_off[N] = tot;
+  __syncthreads();
+  if (blockIdx.x == 0) {
+    if (tid < N) offsets[tid] = s_off[tid];
+    if (tid == 0) offsets[N] = tot;
+  }
+  const int64_t f = (int64_t)blockIdx.x * kPermChunk + tid;
+  if (f >= S) return;
+  const int e = idx[f];
+  const int row = s_off[e] + base[(int64_t)blockIdx.x * N + e] + rank[f];
+  row_token[row] = (int32_t)(f / k);
+  slot_row[f] = row;
+}
+
+hipError_t launch_permute(const int32_t* idx, int64_t T, int k, int N, int32_t* hist,
+                          int32_t* base, int32_t* rank, int32_t* counts, int32_t* offsets,
+                          int32_t* row_token, int32_t* slot_row, hipStream_t stream) {
+  const int64_t S = T * k;
+  const int nchunks = (int)cdiv(S, kPermChunk);
+  permute_hist_kernel<<<(unsigned)cdiv(nchunks, 4), 256, 4 * N * sizeof(int), stream>>>(
+      idx, S, N, nchunks, hist, rank);
+  permute_scan_kernel<<<N, 256, 0, stream>>>(hist, nchunks, N, base, counts);
+  permute_scatter_kernel<<<nchunks, 256, 0, stream>>>(idx, S, k, N, counts, base, rank, offsets,
+                                                      row_token, slot_row);
+  return hipGetLastError();
+}
+
+__global__ void fill_i32_kernel(int32_t* p, int64_t n, int32_t v) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i < n) p[i] = v;
+}
+__global__ void set_range_kernel(int32_t* p, int32_t n) {
+  if (threadIdx.x == 0) {
+    p[0] = 0;
+    p[1] = n;
+  }
+}
+
+hipError_t launch_fill_i32(int32_t* p, int64_t n, int32_t value, hipStream_t stream) {
+  if (n <= 0) return hipSuccess;
+  fill_i32_kernel<<<(unsigned)cdiv(n, 256), 256, 0, stream>>>(p, n, value);
+  return hipGetLastError();
+}
+
+hipError_t launch_set_range(int32_t* p, int32_t n, hipStream_t stream) {
+  set_range_kernel<<<1, 64, 0, stream>>>(p, n);
+  return hipGetLastError();
+}
+
+// x_perm[r] = x[row_token[r]]: one 256-thread block per row, 16-byte copies.
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+__global__ __launch_bounds__(256) void gather_rows_kernel(const u32x4_t* __restrict__ x,
+                                                          const int32_t* __restrict__ row_token,
+                                                          u32x4_t* __restrict__ out,
+                                                          int64_t vec_per_row) {
+  const int64_t r = blockIdx.x;
+  const int64_t src = row_token[r];
+  for (int64_t i = threadIdx.x; i < vec_per_row; i += 256)
+    out[r * vec_per_row + i] = x[src * vec_per_row + i];
+}
+
+hipError_t launch_gather_rows(const void* x, const int32_t* row_token, void* x_perm,
+                              int64_t rows, int64_t row_bytes, hipStream_t stream) {
+  if (rows <= 0) return hipSuccess;
+  gather_rows_kernel<<<(unsigned)rows, 256, 0, stream>>>((const u32x4_t*)x, row_token,
+                                                         (u32x4_t*)x_perm, row_bytes / 16);
+  return hipGetLastError();
+}
+
+}  // namespace moe

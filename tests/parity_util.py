@@ -1,0 +1,74 @@
+"""Helpers shared by the GPU parity tests: oracle runs on seeded inputs and the
+comparison rules (routing bit-exact outside near-ties, outputs relative to the
+oracle output's RMS)."""
+from __future__ import annotations
+
+import sys
+
+import numpy as np
+
+import datagen
+import oracle
+
+TIE = 1e-6  # keys closer than this may legitimately select differently
+TOL = {"f32": 1e-4, "bf16": 2e-2, "fp8": 5e-2}
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def tol_for(cfg) -> float:
+    return TOL[cfg.w_dtype]
+
+
+def rel_err(got: np.ndarray, ref: np.ndarray) -> float:
+    rms = float(np.sqrt(np.mean(np.square(ref)))) if ref.size else 1.0
+    if ref.size == 0:
+        return 0.0
+    return float(np.max(np.abs(got.astype(np.float64) - ref))) / max(rms, 1e-30)
+
+
+def oracle_route(cfg, inp: datagen.MoEInputs, x=None):
+    x = inp.x() if x is None else x
+    x64 = oracle.widen(x, cfg.act_dtype)
+    return oracle.route(cfg, x64, inp.router_w().astype(np.float64), inp.router_b())
+
+
+def check_routing(cfg, r, idx_gpu: np.ndarray, gate_gpu: np.ndarray, gate_tol=2e-5):
+    """Selected sets equal the oracle's except for near-tie tokens, whose
+    selection must still be a valid top-k within the tie window.  Gates are
+    compared per selected expert.  Returns (near_tie_count, order_diffs)."""
+    T, k = idx_gpu.shape
+    idx_o = r["idx"]
+    near = r["margin"] < TIE
+    so, sg = np.sort(idx_o, 1), np.sort(idx_gpu.astype(np.int64), 1)
+    same = np.all(so == sg, axis=1)
+    bad = ~same & ~near
+    assert not bad.any(), (f"{int(bad.sum())} tokens select a different expert set outside the "
+                           f"tie window; first {np.nonzero(bad)[0][:5]}: oracle {idx_o[bad][:2]} "
+                           f"gpu {idx_gpu[bad][:2]} margins {r['margin'][bad][:2]}")
+    # all selections are distinct, in range
+    assert np.all((idx_gpu >= 0) & (idx_gpu < cfg.n_routed))
+    assert np.all(np.diff(sg, axis=1) > 0)
+    # near ties: every GPU pick must have a key within TIE of the k-th key and
+    # lie in a group whose score is within TIE of the last kept group
+    key = r["key"]
+    for t in np.nonzero(near & ~same)[0]:
+        kth = np.sort(key[t][r["allowed"][t]])[::-1][k - 1]
+        assert np.all(key[t][idx_gpu[t]] >= kth - TIE), t
+        if cfg.n_groups > 1:
+            gsc = r["group_scores"][t]
+            gs = cfg.n_routed // cfg.n_groups
+            last = np.sort(gsc)[::-1][cfg.topk_groups - 1]
+            assert np.all(gsc[idx_gpu[t] // gs] >= last - TIE), t
+    # gates of the agreeing tokens, matched by expert id
+    oi = np.argsort(idx_o, 1)
+    gi = np.argsort(idx_gpu, 1)
+    go = np.take_along_axis(r["gates"], oi, 1)[same]
+    gg = np.take_along_axis(gate_gpu.astype(np.float64), gi, 1)[same]
+    err = np.abs(go - gg) / np.maximum(np.abs(go), 1e-3)
+    assert err.max(initial=0) < gate_tol, f"gate rel err {err.max()}"
+    order_diff = int(np.sum(np.any(idx_o[same] != idx_gpu[same], axis=1)))
+    return int(near.sum()), order_diff
