@@ -1,0 +1,262 @@
+"""Benchmark of the MI355X DeepSeekMoE layer forward (one GPU).
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload v3_prefill]
+
+A step is one whole layer forward (router -> permute -> routed experts ->
+shared expert on a second stream -> combine) over one batch of seeded
+synthetic inputs already resident in HBM.  Prints one JSON line:
+
+* value: tokens/s of the V3-shaped prefill (T=16384, d=7168, 1 shared + 256
+  routed experts, top-8 in the top-4 of 8 groups, bf16);
+* roofline: the dominant kernel (the routed W1|W3 grouped GEMM + SwiGLU),
+  timed with HIP events recorded by the library around its launch on the
+  stream it runs on, against the bf16 MFMA peak;
+* decode: the fp8 decode step (T=64) as HBM GB/s over the weights of the
+  experts that receive tokens, and its dominant kernel's roofline;
+* cpu_baseline: the fp64 oracle on the host cores over a bounded sample.
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2516.6  # dense bf16 MFMA, MI355X
+PEAK_HBM_GBPS = 8000.0     # HBM3E
+STAGES = ["router", "permute", "up", "down", "shared_up", "shared_down", "combine"]
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+class HipEvents:
+    """Raw hipEvent_t handles (the HIP runtime torch already loaded)."""
+
+    def __init__(self):
+        self.hip = ctypes.CDLL("libamdhip64.so.7")
+        self.hip.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
+                                                 ctypes.c_void_p]
+        self.hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+
+    def create(self, n):
+        evs = []
+        for _ in range(n):
+            e = ctypes.c_void_p()
+            assert self.hip.hipEventCreate(ctypes.byref(e)) == 0
+            evs.append(e.value)
+        return evs
+
+    def elapsed_ms(self, a, b) -> float:
+        ms = ctypes.c_float()
+        rc = self.hip.hipEventElapsedTime(ctypes.byref(ms), a, b)
+        assert rc == 0, rc
+        return ms.value
+
+    def destroy(self, evs):
+        for e in evs:
+            self.hip.hipEventDestroy(e)
+
+
+def source_digest(*names) -> str:
+    h = hashlib.sha256()
+    for n in names:
+        with open(os.path.join(ROOT, "mixture_experts_ffn_gemm_amd", "csrc", n), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def traffic_from_profile(kernel_key: str, sources, algorithmic_per_launch):
+    """HBM bytes per launch from the committed PMC summary, or None when the
+    kernel's sources changed since the counters were taken."""
+    path = os.path.join(ROOT, "profiles", "pmc_traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        db = json.load(f)
+    ent = db.get(kernel_key)
+    if not ent or ent.get("source_digest") != source_digest(*sources):
+        return None
+    return ent.get("hbm_bytes_per_launch")
+
+
+def run_workload(name, steps, warmup, events: HipEvents):
+    import torch
+    import datagen
+    from datagen.device import upload
+    import mixture_experts_ffn_gemm_amd as moe
+
+    cfg = datagen.get_config(name)
+    t0 = time.time()
+    inp = datagen.MoEInputs(cfg)
+    dev = upload(inp)
+    log(f"[bench] {name}: inputs generated and resident in {time.time() - t0:.1f}s")
+    c = moe.config_from(cfg)
+    ws = moe.Workspace.get(c, "cuda")
+    out = torch.empty((cfg.T, cfg.d), dtype=torch.float32, device="cuda")
+    counts = torch.empty(cfg.n_routed, dtype=torch.int32, device="cuda")
+    main = torch.cuda.current_stream()
+    side = torch.cuda.Stream()
+    L = moe._lib.LIB
+    ex, sh = dev["experts"], dev["shared"] or {}
+    P = lambda t: None if t is None else t.data_ptr()
+    ev_arr_t = ctypes.c_void_p * (2 * len(STAGES))
+    n_ev = 2 * len(STAGES) * steps
+    evs = events.create(n_ev)
+
+    def step(ev_ptr):
+        st = L.moe_forward_timed(
+            c, P(dev["x"]), P(dev["w_r"]), P(dev["b"]), P(ex["w1"]), P(ex["w3"]), P(ex["w2"]),
+            P(ex.get("s1")), P(ex.get("s3")), P(ex.get("s2")), P(sh.get("w1")), P(sh.get("w3")),
+            P(sh.get("w2")), P(sh.get("s1")), P(sh.get("s3")), P(sh.get("s2")), out.data_ptr(),
+            None, None, counts.data_ptr(), ws.data_ptr(), ws.numel(), main.cuda_stream,
+            side.cuda_stream, ev_ptr)
+        if st != 0:
+            raise RuntimeError(f"moe_forward_timed: {moe.status_string(st)}: {moe.last_error()}")
+
+    for _ in range(warmup):
+        step(None)
+    torch.cuda.synchronize()
+    arrays = [ev_arr_t(*evs[i * 2 * len(STAGES):(i + 1) * 2 * len(STAGES)]) for i in range(steps)]
+    torch.cuda.synchronize()
+    t_start = time.perf_counter()
+    for i in range(steps):
+        step(arrays[i])
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t_start
+    stage_ms = {s: [] for s in STAGES}
+    for i in range(steps):
+        base = i * 2 * len(STAGES)
+        for j, s in enumerate(STAGES):
+            if s.startswith("shared") and cfg.n_shared == 0:
+                continue
+            stage_ms[s].append(events.elapsed_ms(evs[base + 2 * j], evs[base + 2 * j + 1]))
+    events.destroy(evs)
+    avg = {s: (sum(v) / len(v) if v else 0.0) for s, v in stage_ms.items()}
+    counts_np = counts.cpu().numpy()
+    res = dict(cfg=cfg, elapsed=elapsed, ms_per_step=elapsed / steps * 1e3, stage_ms=avg,
+               counts=counts_np, inputs=inp)
+    del dev, out
+    torch.cuda.empty_cache()
+    return res
+
+
+def prefill_roofline(r):
+    cfg = r["cfg"]
+    flops = 2.0 * cfg.T * cfg.k * cfg.d * 2 * cfg.inter  # W1 and W3 over all T*k routed rows
+    ms = r["stage_ms"]["up"]
+    achieved = flops / (ms * 1e-3) / 1e12
+    return {"bound": "mfma", "kernel": "gemm_bf16_grouped_kernel<SwiGLU> (routed W1|W3 + SwiGLU)",
+            "achieved": round(achieved, 1), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+            "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+            "algorithmic_per_launch": flops, "avg_launch_ms": round(ms, 4),
+            "traffic": traffic_from_profile("prefill_up", ["gemm_bf16.hip", "grouped_sched.h"], flops)}
+
+
+def decode_summary(r):
+    cfg = r["cfg"]
+    counts = r["counts"]
+    n_active = int((counts > 0).sum())
+    per_expert = cfg.expert_weight_bytes()  # fp8 W1, W3, W2 + fp32 block scales
+    total_bytes = (n_active + cfg.n_shared) * per_expert
+    ms = r["ms_per_step"]
+    gbps = total_bytes / (ms * 1e-3) / 1e9
+    # dominant kernel: routed fp8 W1|W3 stream (2/3 of the active weight bytes)
+    up_bytes = n_active * (2 * cfg.d * cfg.inter + 2 * (cfg.d // 128) * (cfg.inter // 128) * 4)
+    up_ms = r["stage_ms"]["up"]
+    up_gbps = up_bytes / (up_ms * 1e-3) / 1e9
+    return {
+        "workload": cfg.name, "T": cfg.T, "ms_per_step": round(ms, 4),
+        "hbm_GBps": round(gbps, 1), "hbm_frac": round(gbps / PEAK_HBM_GBPS, 4),
+        "n_active_routed": n_active, "idle_experts": int(cfg.n_routed - n_active),
+        "weight_bytes_per_step": total_bytes, "stage_ms": {k: round(v, 4) for k, v in r["stage_ms"].items()},
+        "roofline": {"bound": "hbm", "kernel": "gemm_fp8_small_kernel<SwiGLU> (routed W1|W3 fp8)",
+                     "achieved": round(up_gbps, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
+                     "frac": round(up_gbps / PEAK_HBM_GBPS, 4), "algorithmic_per_launch": up_bytes,
+                     "avg_launch_ms": round(up_ms, 4),
+                     "traffic": traffic_from_profile("decode_up", ["gemm_fp8.hip", "grouped_sched.h"],
+                                                     up_bytes)},
+    }
+
+
+def cpu_baseline(inp, sample_tokens=8):
+    """The fp64 oracle (unchanged) on the first `sample_tokens` tokens of the
+    workload: routing of those tokens plus their routed and shared experts."""
+    import numpy as np
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max((i.get("num_threads", 1) for i in threadpool_info()), default=1)
+    except Exception:
+        threads = len(os.sched_getaffinity(0))
+    cfg = inp.cfg.replace(T=sample_tokens)
+    sub = type(inp)(cfg)  # the same seeds: rows 0..sample-1 of x are identical
+    x = sub.x()
+    wr, b = sub.router_w(), sub.router_b()
+    # generation is excluded from the timing: pre-draw the experts these tokens use
+    r = oracle.route(cfg, oracle.widen(x, cfg.act_dtype), wr.astype(np.float64), b)
+    needed = sorted(set(int(e) for e in np.unique(r["idx"])))
+    cache = {e: sub.expert(e) for e in needed}
+    shared = sub.shared()
+    t0 = time.perf_counter()
+    oracle.forward(cfg, x, wr, b, lambda e: cache[e], shared)
+    dt = time.perf_counter() - t0
+    return {"value": round(sample_tokens / dt, 4), "unit": "tokens/s", "cores": threads,
+            "kind": "oracle",
+            "sample": f"first {sample_tokens} tokens of {inp.cfg.name} (T={inp.cfg.T}): fp64 routing "
+                      f"and {len(needed)} routed experts + shared MLP, {dt:.1f}s"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="v3_prefill")
+    ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (the layer is built and measured on a single "
+              f"MI355X); --gpus {args.gpus} is not supported", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    events = HipEvents()
+    r = run_workload(args.workload, args.steps, args.warmup, events)
+    cfg = r["cfg"]
+    value = cfg.T * args.steps / r["elapsed"]
+    flops = cfg.flops_per_token() * cfg.T
+    line = {
+        "metric": "MoE-layer fwd tokens/s + MFMA % peak (V3 shape); decode HBM GB/s % peak",
+        "value": round(value, 1), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(r["ms_per_step"], 4), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": cfg.w_dtype, "data": "synthetic",
+        "config": {"workload": cfg.name, "T": cfg.T, "d": cfg.d, "n_routed": cfg.n_routed,
+                   "n_shared": cfg.n_shared, "inter": cfg.inter, "k": cfg.k,
+                   "groups": f"{cfg.topk_groups}/{cfg.n_groups}", "gate": cfg.gate},
+        "layer_mfma_frac": round(flops / (r["ms_per_step"] * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+        "stage_ms": {k: round(v, 4) for k, v in r["stage_ms"].items()},
+        "roofline": prefill_roofline(r),
+    }
+    inp = r.pop("inputs")
+    if not args.no_decode:
+        d = run_workload("v3_decode", args.steps, args.warmup, events)
+        d.pop("inputs")
+        line["decode"] = decode_summary(d)
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(inp)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -192,6 +192,35 @@ int moe_forward(const moe_config* cfg, const void* x, const float* W_r, const fl
                 void* out, int32_t* topk_idx_out, float* topk_gate_out, int32_t* counts_out,
                 void* ws, size_t ws_bytes, void* stream_main, void* stream_side);
 
+/* Stages of moe_forward, in launch order (shared ones run on stream_side). */
+typedef enum {
+  MOE_STAGE_ROUTER = 0,      /* logits + selection                 (stream_main) */
+  MOE_STAGE_PERMUTE = 1,     /* histogram, scan, scatter           (stream_main) */
+  MOE_STAGE_UP = 2,          /* routed W1|W3 grouped GEMM + SwiGLU (stream_main) */
+  MOE_STAGE_DOWN = 3,        /* routed W2 grouped GEMM             (stream_main) */
+  MOE_STAGE_SHARED_UP = 4,   /* shared W1|W3 GEMM + SwiGLU         (stream_side) */
+  MOE_STAGE_SHARED_DOWN = 5, /* shared W2 GEMM                     (stream_side) */
+  MOE_STAGE_COMBINE = 6,     /* gate-weighted combine + residual   (stream_main) */
+  MOE_NUM_STAGES = 7
+} moe_stage;
+
+/*
+ * moe_forward_timed - moe_forward that also records caller-owned HIP events
+ * around each stage, for measurement.  stage_events holds 2*MOE_NUM_STAGES
+ * hipEvent_t values passed as void* (NULL entries are skipped): entry 2*s is
+ * recorded just before stage s's first launch and entry 2*s+1 just after its
+ * last, on the stream that stage runs on.  Results are identical to
+ * moe_forward.
+ */
+int moe_forward_timed(const moe_config* cfg, const void* x, const float* W_r, const float* b,
+                      const void* W1, const void* W3, const void* W2,
+                      const float* s1, const float* s3, const float* s2,
+                      const void* W1s, const void* W3s, const void* W2s,
+                      const float* s1s, const float* s3s, const float* s2s,
+                      void* out, int32_t* topk_idx_out, float* topk_gate_out, int32_t* counts_out,
+                      void* ws, size_t ws_bytes, void* stream_main, void* stream_side,
+                      void* const* stage_events);
+
 #ifdef __cplusplus
 }
 #endif

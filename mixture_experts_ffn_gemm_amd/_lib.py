@@ -20,7 +20,8 @@ GATES = {"softmax": 0, "sigmoid": 1}
 
 # every symbol include/moe.h declares
 EXPORTS = ["moe_status_string", "moe_last_error", "moe_version", "moe_workspace_size",
-           "moe_router", "moe_permute", "moe_expert_ffn", "moe_combine", "moe_forward"]
+           "moe_router", "moe_permute", "moe_expert_ffn", "moe_combine", "moe_forward",
+           "moe_forward_timed"]
 
 
 class MoeConfig(ctypes.Structure):
@@ -61,6 +62,8 @@ def _load():
     lib.moe_combine.argtypes = [POINTER(MoeConfig), P, P, P, P, P, P, P]
     lib.moe_forward.restype = ctypes.c_int
     lib.moe_forward.argtypes = [POINTER(MoeConfig)] + [P] * 20 + [c_size_t, P, P]
+    lib.moe_forward_timed.restype = ctypes.c_int
+    lib.moe_forward_timed.argtypes = [POINTER(MoeConfig)] + [P] * 20 + [c_size_t, P, P, P]
     return lib
 
 

@@ -115,6 +115,13 @@ int check_ws(const moe_config* c, void* ws, size_t ws_bytes) {
   return MOE_OK;
 }
 
+// Records stage event 2*stage (+1 for the end) when the caller supplied it.
+hipError_t mark(void* const* ev, int stage, bool end, hipStream_t s) {
+  if (!ev || stage < 0) return hipSuccess;
+  void* e = ev[2 * stage + (end ? 1 : 0)];
+  return e ? hipEventRecord((hipEvent_t)e, s) : hipSuccess;
+}
+
 template <typename P>
 P* at(void* ws, size_t off) {
   return (P*)((char*)ws + off);
@@ -134,7 +141,8 @@ int run_router(const moe_config* c, const void* x, const float* W_r, const float
 int run_expert_ffn(const moe_config* c, int n_experts, const int32_t* offsets, int64_t max_rows,
                    int inter, const void* x_rows, const int32_t* row_index, const void* W1,
                    const void* W3, const void* W2, const float* s1, const float* s3,
-                   const float* s2, void* h, void* y_rows, hipStream_t s) {
+                   const float* s2, void* h, void* y_rows, hipStream_t s,
+                   void* const* ev = nullptr, int stage_up = -1, int stage_dn = -1) {
   GroupedGemmArgs up{};
   up.A = x_rows;
   up.row_index = row_index;
@@ -161,16 +169,22 @@ int run_expert_ffn(const moe_config* c, int n_experts, const int32_t* offsets, i
   dn.C = y_rows;
   dn.Nout = c->d;
   dn.K = inter;
-  if (c->w_dtype == MOE_F32) {
+  MOE_HIP_CHECK(mark(ev, stage_up, false, s));
+  if (c->w_dtype == MOE_F32)
     MOE_HIP_CHECK(launch_gemm_f32_swiglu(up, s));
-    MOE_HIP_CHECK(launch_gemm_f32_store(dn, s));
-  } else if (c->w_dtype == MOE_BF16) {
+  else if (c->w_dtype == MOE_BF16)
     MOE_HIP_CHECK(launch_gemm_bf16_swiglu(up, s));
-    MOE_HIP_CHECK(launch_gemm_bf16_store(dn, s));
-  } else {
+  else
     MOE_HIP_CHECK(launch_gemm_fp8_swiglu(up, s));
+  MOE_HIP_CHECK(mark(ev, stage_up, true, s));
+  MOE_HIP_CHECK(mark(ev, stage_dn, false, s));
+  if (c->w_dtype == MOE_F32)
+    MOE_HIP_CHECK(launch_gemm_f32_store(dn, s));
+  else if (c->w_dtype == MOE_BF16)
+    MOE_HIP_CHECK(launch_gemm_bf16_store(dn, s));
+  else
     MOE_HIP_CHECK(launch_gemm_fp8_store(dn, s));
-  }
+  MOE_HIP_CHECK(mark(ev, stage_dn, true, s));
   return MOE_OK;
 }
 
@@ -282,12 +296,13 @@ int moe_combine(const moe_config* cfg, const void* y_perm, const int32_t* slot_r
   return MOE_OK;
 }
 
-int moe_forward(const moe_config* cfg, const void* x, const float* W_r, const float* b,
-                const void* W1, const void* W3, const void* W2, const float* s1, const float* s3,
-                const float* s2, const void* W1s, const void* W3s, const void* W2s,
-                const float* s1s, const float* s3s, const float* s2s, void* out,
-                int32_t* topk_idx_out, float* topk_gate_out, int32_t* counts_out, void* ws,
-                size_t ws_bytes, void* stream_main, void* stream_side) {
+static int forward_impl(const moe_config* cfg, const void* x, const float* W_r, const float* b,
+                        const void* W1, const void* W3, const void* W2, const float* s1,
+                        const float* s3, const float* s2, const void* W1s, const void* W3s,
+                        const void* W2s, const float* s1s, const float* s3s, const float* s2s,
+                        void* out, int32_t* topk_idx_out, float* topk_gate_out,
+                        int32_t* counts_out, void* ws, size_t ws_bytes, void* stream_main,
+                        void* stream_side, void* const* ev) {
   g_err.clear();
   int st = check_config(cfg);
   if (st) return st;
@@ -333,7 +348,8 @@ int moe_forward(const moe_config* cfg, const void* x, const float* W_r, const fl
     ys = at<void>(ws, L.ys);
     MOE_HIP_CHECK(launch_set_range(shoff, (int32_t)c.T, ss));
     st = run_expert_ffn(cfg, 1, shoff, c.T, c.n_shared * c.inter, x, nullptr, W1s, W3s, W2s, s1s,
-                        s3s, s2s, at<void>(ws, L.hs), ys, ss);
+                        s3s, s2s, at<void>(ws, L.hs), ys, ss, ev, MOE_STAGE_SHARED_UP,
+                        MOE_STAGE_SHARED_DOWN);
     if (st) return st;
     if (two_streams) MOE_HIP_CHECK(hipEventRecord(ev_join, ss));
   }
@@ -344,18 +360,47 @@ int moe_forward(const moe_config* cfg, const void* x, const float* W_r, const fl
   int32_t* offsets = at<int32_t>(ws, L.offsets);
   int32_t* row_token = at<int32_t>(ws, L.row_token);
   int32_t* slot_row = at<int32_t>(ws, L.slot_row);
+  MOE_HIP_CHECK(mark(ev, MOE_STAGE_ROUTER, false, sm));
   if ((st = run_router(cfg, x, W_r, b, idx, gate, nullptr, ws, sm))) return st;
+  MOE_HIP_CHECK(mark(ev, MOE_STAGE_ROUTER, true, sm));
+  MOE_HIP_CHECK(mark(ev, MOE_STAGE_PERMUTE, false, sm));
   MOE_HIP_CHECK(launch_permute(idx, c.T, c.k, c.n_routed, at<int32_t>(ws, L.hist),
                                at<int32_t>(ws, L.base), at<int32_t>(ws, L.rank), counts, offsets,
                                row_token, slot_row, sm));
+  MOE_HIP_CHECK(mark(ev, MOE_STAGE_PERMUTE, true, sm));
   void* y = at<void>(ws, L.y);
   st = run_expert_ffn(cfg, c.n_routed, offsets, c.T * c.k, c.inter, x, row_token, W1, W3, W2, s1,
-                      s3, s2, at<void>(ws, L.h), y, sm);
+                      s3, s2, at<void>(ws, L.h), y, sm, ev, MOE_STAGE_UP, MOE_STAGE_DOWN);
   if (st) return st;
   if (two_streams) MOE_HIP_CHECK(hipStreamWaitEvent(sm, ev_join, 0));
+  MOE_HIP_CHECK(mark(ev, MOE_STAGE_COMBINE, false, sm));
   MOE_HIP_CHECK(launch_combine(c.act_dtype == MOE_BF16, c.out_dtype == MOE_BF16, y, slot_row, gate,
                                ys, x, out, c.T, c.d, c.k, sm));
+  MOE_HIP_CHECK(mark(ev, MOE_STAGE_COMBINE, true, sm));
   return MOE_OK;
+}
+
+int moe_forward(const moe_config* cfg, const void* x, const float* W_r, const float* b,
+                const void* W1, const void* W3, const void* W2, const float* s1, const float* s3,
+                const float* s2, const void* W1s, const void* W3s, const void* W2s,
+                const float* s1s, const float* s3s, const float* s2s, void* out,
+                int32_t* topk_idx_out, float* topk_gate_out, int32_t* counts_out, void* ws,
+                size_t ws_bytes, void* stream_main, void* stream_side) {
+  return forward_impl(cfg, x, W_r, b, W1, W3, W2, s1, s3, s2, W1s, W3s, W2s, s1s, s3s, s2s, out,
+                      topk_idx_out, topk_gate_out, counts_out, ws, ws_bytes, stream_main,
+                      stream_side, nullptr);
+}
+
+int moe_forward_timed(const moe_config* cfg, const void* x, const float* W_r, const float* b,
+                      const void* W1, const void* W3, const void* W2, const float* s1,
+                      const float* s3, const float* s2, const void* W1s, const void* W3s,
+                      const void* W2s, const float* s1s, const float* s3s, const float* s2s,
+                      void* out, int32_t* topk_idx_out, float* topk_gate_out,
+                      int32_t* counts_out, void* ws, size_t ws_bytes, void* stream_main,
+                      void* stream_side, void* const* stage_events) {
+  return forward_impl(cfg, x, W_r, b, W1, W3, W2, s1, s3, s2, W1s, W3s, W2s, s1s, s3s, s2s, out,
+                      topk_idx_out, topk_gate_out, counts_out, ws, ws_bytes, stream_main,
+                      stream_side, stage_events);
 }
 
 }  // extern "C"

@@ -30,6 +30,20 @@ def rel_err(got: np.ndarray, ref: np.ndarray) -> float:
     return float(np.max(np.abs(got.astype(np.float64) - ref))) / max(rms, 1e-30)
 
 
+def bf16_floor(ref: np.ndarray) -> float:
+    """max |bf16(ref) - ref| / RMS(ref): the error a bf16 output has even when
+    every value is the correctly rounded oracle value."""
+    import torch
+    r16 = torch.from_numpy(ref.astype(np.float32)).to(torch.bfloat16).double().numpy()
+    return rel_err(r16, ref)
+
+
+def bf16_half_ulp(v: np.ndarray) -> np.ndarray:
+    """Half a bf16 ulp at |v| (8 significant bits)."""
+    e = np.floor(np.log2(np.maximum(np.abs(v), 2.0 ** -126)))
+    return 2.0 ** (e - 8)
+
+
 def oracle_route(cfg, inp: datagen.MoEInputs, x=None):
     x = inp.x() if x is None else x
     x64 = oracle.widen(x, cfg.act_dtype)

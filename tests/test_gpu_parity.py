@@ -11,7 +11,8 @@ import torch
 import datagen
 import oracle
 from datagen.device import upload, to_torch
-from parity_util import TIE, check_routing, oracle_route, rel_err, say, tol_for
+from parity_util import (TIE, bf16_floor, bf16_half_ulp, check_routing, oracle_route, rel_err,
+                         say, tol_for)
 
 pytestmark = [pytest.mark.gpu, pytest.mark.filterwarnings("ignore::RuntimeWarning")]
 
@@ -151,8 +152,11 @@ def test_expert_ffn_ragged_groups(lib, wdt):
         w = oracle.expert_weights64(cfg, {k: (v[e] if v is not None else None) for k, v in ex.items()})
         ref[off[e]:off[e + 1]] = oracle.swiglu(x64[off[e]:off[e + 1]], *w)
     err = rel_err(got, ref)
-    say(f"   rel err {err:.3e}")
-    assert err < tol_for(cfg) / 2
+    floor = bf16_floor(ref) if cfg.act_dtype == "bf16" else 0.0
+    say(f"   rel err {err:.3e} (bf16 output rounding alone: {floor:.3e})")
+    assert err < tol_for(cfg)
+    # beyond the output rounding, only the bf16 rounding of h and fp32 sums
+    assert err <= floor + (5e-3 if cfg.act_dtype == "bf16" else 2e-5)
 
 
 # ---------------------------------------------------------------- combine
@@ -180,9 +184,13 @@ def test_combine(lib, act, out):
     g = gate.double().cpu().numpy()
     delta = np.einsum("tk,tkd->td", g, yp[sr])
     ref = delta + y_sh.double().cpu().numpy() + x.double().cpu().numpy()
-    tol = 1e-6 if out == "f32" else 2 ** -8
-    assert rel_err(o.double().cpu().numpy(), ref) < tol
-    assert rel_err(o2.double().cpu().numpy(), delta) < tol
+    if out == "f32":
+        assert rel_err(o.double().cpu().numpy(), ref) < 1e-6
+        assert rel_err(o2.double().cpu().numpy(), delta) < 1e-6
+    else:  # one rounding of the fp32 sum: within half a bf16 ulp (+ fp32 slack)
+        for got, want in ((o, ref), (o2, delta)):
+            g = got.double().cpu().numpy()
+            assert np.all(np.abs(g - want) <= bf16_half_ulp(want) + 1e-5 * np.abs(want) + 1e-30)
 
 
 # ---------------------------------------------------------------- forward
