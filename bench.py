@@ -215,7 +215,29 @@ def cpu_baseline(inp, sample_tokens=8):
                       f"and {len(needed)} routed experts + shared MLP, {dt:.1f}s"}
 
 
+def summarize_trace(path, title=""):
+    """Print a per-kernel table (calls, average and total duration, grouped by
+    kernel and grid size) of a rocprofv3 kernel-trace CSV."""
+    import collections
+    import csv
+    rows = list(csv.DictReader(open(path)))
+    agg = collections.defaultdict(list)
+    for r in rows:
+        dur = int(r["End_Timestamp"]) - int(r["Start_Timestamp"])
+        agg[(r["Kernel_Name"], r.get("Grid_Size", ""))].append(dur)
+    total = sum(sum(v) for v in agg.values()) or 1
+    if title:
+        print(title)
+    print(f"{'kernel':100s} {'grid':>9s} {'calls':>6s} {'avg_us':>10s} {'total_ms':>10s} {'pct':>6s}")
+    for (name, grid), v in sorted(agg.items(), key=lambda kv: -sum(kv[1])):
+        print(f"{name[:100]:100s} {grid:>9s} {len(v):6d} {sum(v) / len(v) / 1e3:10.2f} "
+              f"{sum(v) / 1e6:10.3f} {100 * sum(v) / total:6.2f}")
+
+
 def main():
+    if len(sys.argv) > 1 and sys.argv[1] == "--summarize-trace":
+        summarize_trace(sys.argv[2], sys.argv[3] if len(sys.argv) > 3 else "")
+        return
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)

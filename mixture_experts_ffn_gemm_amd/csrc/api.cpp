@@ -30,7 +30,7 @@ size_t act_bytes(int dt) { return dt == MOE_F32 ? 4 : 2; }
 size_t align_up(size_t v) { return (v + 255) & ~size_t(255); }
 
 struct Layout {
-  size_t z, wr3, idx, gate, hist, base, rank, counts, offsets, row_token, slot_row, h, y, hs, ys,
+  size_t z, idx, gate, hist, base, rank, counts, offsets, row_token, slot_row, h, y, hs, ys,
       shoff, total;
   int64_t h_elems;  // capacity of the h region in activation elements
 };
@@ -47,8 +47,8 @@ Layout make_layout(const moe_config& c) {
   const int64_t slots = T * c.k;
   const int64_t nchunks = cdiv(slots, kPermChunk);
   const size_t as = act_bytes(c.act_dtype);
-  L.z = take(T * N * 4);
-  L.wr3 = take(N * 3 * d * 2);
+  const int64_t nsplit = c.act_dtype == MOE_BF16 ? router_mfma_splits(T, c.d, c.n_routed) : 1;
+  L.z = take(nsplit * T * N * 4);
   L.idx = take(slots * 4);
   L.gate = take(slots * 4);
   L.hist = take(nchunks * N * 4);
@@ -131,9 +131,15 @@ int run_router(const moe_config* c, const void* x, const float* W_r, const float
                int32_t* idx, float* gate, float* scores, void* ws, hipStream_t s) {
   const Layout L = make_layout(*c);
   float* z = at<float>(ws, L.z);
-  MOE_HIP_CHECK(launch_router_logits_simt(c->act_dtype == MOE_BF16, x, W_r, z, c->T, c->d,
-                                          c->n_routed, s));
-  MOE_HIP_CHECK(launch_router_select(z, b, c->T, c->n_routed, c->k, c->n_groups, c->topk_groups,
+  int nsplit = 1;
+  if (c->act_dtype == MOE_BF16) {
+    nsplit = router_mfma_splits(c->T, c->d, c->n_routed);
+    MOE_HIP_CHECK(launch_router_logits_mfma((const bf16_t*)x, W_r, z, c->T, c->d, c->n_routed,
+                                            nsplit, s));
+  } else {
+    MOE_HIP_CHECK(launch_router_logits_simt(false, x, W_r, z, c->T, c->d, c->n_routed, s));
+  }
+  MOE_HIP_CHECK(launch_router_select(z, nsplit, b, c->T, c->n_routed, c->k, c->n_groups, c->topk_groups,
                                      c->group_topn, c->gate, c->route_scale, idx, gate, scores, s));
   return MOE_OK;
 }
@@ -173,7 +179,7 @@ int run_expert_ffn(const moe_config* c, int n_experts, const int32_t* offsets, i
   if (c->w_dtype == MOE_F32)
     MOE_HIP_CHECK(launch_gemm_f32_swiglu(up, s));
   else if (c->w_dtype == MOE_BF16)
-    MOE_HIP_CHECK(launch_gemm_bf16_swiglu(up, s));
+    MOE_HIP_CHECK(launch_gemm_bf16_v2(up, true, s));
   else
     MOE_HIP_CHECK(launch_gemm_fp8_swiglu(up, s));
   MOE_HIP_CHECK(mark(ev, stage_up, true, s));
@@ -181,7 +187,7 @@ int run_expert_ffn(const moe_config* c, int n_experts, const int32_t* offsets, i
   if (c->w_dtype == MOE_F32)
     MOE_HIP_CHECK(launch_gemm_f32_store(dn, s));
   else if (c->w_dtype == MOE_BF16)
-    MOE_HIP_CHECK(launch_gemm_bf16_store(dn, s));
+    MOE_HIP_CHECK(launch_gemm_bf16_v2(dn, false, s));
   else
     MOE_HIP_CHECK(launch_gemm_fp8_store(dn, s));
   MOE_HIP_CHECK(mark(ev, stage_dn, true, s));

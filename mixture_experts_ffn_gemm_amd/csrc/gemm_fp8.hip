@@ -35,30 +35,24 @@ __device__ __forceinline__ bf16x8_t fp8x8_to_bf16(uint32_t w0, uint32_t w1) {
   return bf16x8_t{p0[0], p0[1], p1[0], p1[1], p2[0], p2[1], p3[0], p3[1]};
 }
 
-template <bool SWIGLU>
-__global__ __launch_bounds__(256) void gemm_fp8_small_kernel(GroupedGemmArgs args) {
-  constexpr int BM = 64, BN = 64, NCH = BM / 16;
+// K loop + epilogue for NC valid 16-row chunks.  PF k-blocks (128 values of K)
+// of this lane's weights are kept in flight in a register ring.
+template <bool SWIGLU, int NC, int PF>
+__device__ __forceinline__ void fp8_tile(const GroupedGemmArgs& args, const TileCoord& tc,
+                                         int nrows) {
   constexpr int NB = SWIGLU ? 2 : 1;
-  __shared__ int s_ts[kMaxGroups + 1];
-  __shared__ int s_scratch[4];
-  __shared__ int s_info[1];
-  TileCoord tc;
-  if (!grouped_tile_lookup<256>(args.offsets, args.n_groups, BM, BN, args.Nout, s_ts, s_scratch,
-                                s_info, &tc))
-    return;
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int col = lane & 15, kg = lane >> 4;
   const int K = args.K, Nout = args.Nout, KB = K / 128;
-  const int64_t nrows_ = tc.rend - tc.row0;
-  const int nrows = nrows_ < BM ? (int)nrows_ : BM;
-  const int nch = (nrows + 15) >> 4;
   const int ncol0 = tc.n0 + wv * 16;
 
   const uint8_t* bp[NB];
   const float* sp[NB];
   {
-    const int64_t boff = ((int64_t)tc.group * Nout + ncol0 + col) * K + kg * 16;
-    const int64_t soff = ((int64_t)tc.group * (Nout / 128) + ncol0 / 128) * KB;
+    int n = ncol0 + col;
+    if (n > Nout - 1) n = Nout - 1;
+    const int64_t boff = ((int64_t)tc.group * Nout + n) * K + kg * 16;
+    const int64_t soff = ((int64_t)tc.group * (Nout / 128) + (n >> 7)) * KB;
     bp[0] = (const uint8_t*)args.B0 + boff;
     sp[0] = args.S0 + soff;
     if (SWIGLU) {
@@ -66,87 +60,118 @@ __global__ __launch_bounds__(256) void gemm_fp8_small_kernel(GroupedGemmArgs arg
       sp[NB - 1] = args.S1 + soff;
     }
   }
-  const bf16_t* ap[NCH];
+  const bf16_t* ap[NC];
 #pragma unroll
-  for (int c = 0; c < NCH; ++c) {
+  for (int c = 0; c < NC; ++c) {
     int64_t r = tc.row0 + c * 16 + col;
     if (r > tc.rend - 1) r = tc.rend - 1;
     const int64_t src = args.row_index ? (int64_t)args.row_index[r] : r;
     ap[c] = (const bf16_t*)args.A + src * K + kg * 16;
   }
 
-  f32x4_t acc[NB][NCH];
+  f32x4_t acc[NB][NC];
 #pragma unroll
   for (int m = 0; m < NB; ++m)
 #pragma unroll
-    for (int c = 0; c < NCH; ++c) acc[m][c] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    for (int c = 0; c < NC; ++c) acc[m][c] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-  u32x4_t bnext[NB][2];
+  u32x4_t ring[PF][NB][2];
 #pragma unroll
-  for (int m = 0; m < NB; ++m)
-#pragma unroll
-    for (int h = 0; h < 2; ++h) bnext[m][h] = *(const u32x4_t*)(bp[m] + h * 64);
-
-  for (int kb = 0; kb < KB; ++kb) {
-    u32x4_t bcur[NB][2];
-#pragma unroll
-    for (int m = 0; m < NB; ++m)
-#pragma unroll
-      for (int h = 0; h < 2; ++h) bcur[m][h] = bnext[m][h];
-    if (kb + 1 < KB) {
+  for (int p = 0; p < PF; ++p)
+    if (p < KB) {
 #pragma unroll
       for (int m = 0; m < NB; ++m)
 #pragma unroll
-        for (int h = 0; h < 2; ++h)
-          bnext[m][h] = *(const u32x4_t*)(bp[m] + (kb + 1) * 128 + h * 64);
+        for (int h = 0; h < 2; ++h) ring[p][m][h] = *(const u32x4_t*)(bp[m] + p * 128 + h * 64);
     }
-    f32x4_t tmp[NB][NCH];
+
+  for (int kb0 = 0; kb0 < KB; kb0 += PF) {
 #pragma unroll
-    for (int m = 0; m < NB; ++m)
+    for (int p = 0; p < PF; ++p) {
+      const int kb = kb0 + p;
+      if (kb < KB) {
+        u32x4_t cur[NB][2];
 #pragma unroll
-      for (int c = 0; c < NCH; ++c) tmp[m][c] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        for (int m = 0; m < NB; ++m)
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      const int k0 = kb * 128 + h * 64;
-      bf16x8_t blo[NB], bhi[NB];
+          for (int h = 0; h < 2; ++h) cur[m][h] = ring[p][m][h];
+        if (kb + PF < KB) {
 #pragma unroll
-      for (int m = 0; m < NB; ++m) {
-        blo[m] = fp8x8_to_bf16(bcur[m][h][0], bcur[m][h][1]);
-        bhi[m] = fp8x8_to_bf16(bcur[m][h][2], bcur[m][h][3]);
-      }
+          for (int m = 0; m < NB; ++m)
 #pragma unroll
-      for (int c = 0; c < NCH; ++c) {
-        if (c < nch) {
-          const bf16x8_t alo = *(const bf16x8_t*)(ap[c] + k0);
-          const bf16x8_t ahi = *(const bf16x8_t*)(ap[c] + k0 + 8);
+            for (int h = 0; h < 2; ++h)
+              ring[p][m][h] = *(const u32x4_t*)(bp[m] + (kb + PF) * 128 + h * 64);
+        }
+        float sc[NB];
+#pragma unroll
+        for (int m = 0; m < NB; ++m) sc[m] = sp[m][kb];
+        f32x4_t tmp[NB][NC];
+#pragma unroll
+        for (int m = 0; m < NB; ++m)
+#pragma unroll
+          for (int c = 0; c < NC; ++c) tmp[m][c] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          const int k0 = kb * 128 + h * 64;
+          bf16x8_t blo[NB], bhi[NB];
 #pragma unroll
           for (int m = 0; m < NB; ++m) {
-            tmp[m][c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(alo, blo[m], tmp[m][c], 0, 0, 0);
-            tmp[m][c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ahi, bhi[m], tmp[m][c], 0, 0, 0);
+            blo[m] = fp8x8_to_bf16(cur[m][h][0], cur[m][h][1]);
+            bhi[m] = fp8x8_to_bf16(cur[m][h][2], cur[m][h][3]);
+          }
+#pragma unroll
+          for (int c = 0; c < NC; ++c) {
+            const bf16x8_t alo = *(const bf16x8_t*)(ap[c] + k0);
+            const bf16x8_t ahi = *(const bf16x8_t*)(ap[c] + k0 + 8);
+#pragma unroll
+            for (int m = 0; m < NB; ++m) {
+              tmp[m][c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(alo, blo[m], tmp[m][c], 0, 0, 0);
+              tmp[m][c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ahi, bhi[m], tmp[m][c], 0, 0, 0);
+            }
           }
         }
+#pragma unroll
+        for (int m = 0; m < NB; ++m)
+#pragma unroll
+          for (int c = 0; c < NC; ++c) acc[m][c] += tmp[m][c] * sc[m];
       }
-    }
-#pragma unroll
-    for (int m = 0; m < NB; ++m) {
-      const float s = sp[m][kb];
-#pragma unroll
-      for (int c = 0; c < NCH; ++c) acc[m][c] += tmp[m][c] * s;
     }
   }
 
   bf16_t* __restrict__ C = (bf16_t*)args.C;
+  const int ocol = ncol0 + col;
+  if (ocol >= Nout) return;
 #pragma unroll
-  for (int c = 0; c < NCH; ++c) {
-    if (c >= nch) continue;
+  for (int c = 0; c < NC; ++c) {
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const int row = c * 16 + 4 * kg + r;
       if (row >= nrows) continue;
       float v = acc[0][c][r];
       if (SWIGLU) v = v / (1.f + __expf(-v)) * acc[NB - 1][c][r];
-      C[(tc.row0 + row) * Nout + ncol0 + col] = f32_to_bf16(v);
+      C[(tc.row0 + row) * Nout + ocol] = f32_to_bf16(v);
     }
+  }
+}
+
+template <bool SWIGLU>
+__global__ __launch_bounds__(256) void gemm_fp8_small_kernel(GroupedGemmArgs args) {
+  constexpr int BM = 64, BN = 64;
+  constexpr int PF = SWIGLU ? 4 : 8;
+  __shared__ int s_ts[kMaxGroups + 1];
+  __shared__ int s_scratch[4];
+  __shared__ int s_info[1];
+  TileCoord tc;
+  if (!grouped_tile_lookup<256>(args.offsets, args.n_groups, BM, BN, args.Nout, s_ts, s_scratch,
+                                s_info, &tc))
+    return;
+  const int64_t nrows_ = tc.rend - tc.row0;
+  const int nrows = nrows_ < BM ? (int)nrows_ : BM;
+  switch ((nrows + 15) >> 4) {
+    case 1: fp8_tile<SWIGLU, 1, PF>(args, tc, nrows); break;
+    case 2: fp8_tile<SWIGLU, 2, PF>(args, tc, nrows); break;
+    case 3: fp8_tile<SWIGLU, 3, PF>(args, tc, nrows); break;
+    default: fp8_tile<SWIGLU, 4, PF>(args, tc, nrows); break;
   }
 }
 

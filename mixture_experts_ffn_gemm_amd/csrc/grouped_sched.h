@@ -46,7 +46,7 @@ __device__ __forceinline__ bool grouped_tile_lookup(const int32_t* __restrict__ 
   const int incl = block_incl_scan<NT>(tiles, s_scratch, &total_m);
   if (tid < n_groups) s_ts[tid + 1] = incl;
   if (tid == 0) s_ts[0] = 0;
-  const int n_tiles_n = Nout / BN;
+  const int n_tiles_n = (Nout + BN - 1) / BN;
   const int total = total_m * n_tiles_n;
   const int per = (total + kNumXcd - 1) / kNumXcd;
   const int w = blockIdx.x;
@@ -74,7 +74,7 @@ __device__ __forceinline__ bool grouped_tile_lookup(const int32_t* __restrict__ 
 // Upper bound of the number of workgroups a grouped launch needs.
 inline int64_t grouped_grid(int64_t max_rows, int n_groups, int BM, int BN, int Nout) {
   const int64_t mt = max_rows / BM + n_groups;
-  const int64_t n = mt * (Nout / BN);
+  const int64_t n = mt * ((Nout + BN - 1) / BN);
   return ((n + kNumXcd - 1) / kNumXcd) * kNumXcd;
 }
 

@@ -38,14 +38,14 @@ __host__ __device__ inline int64_t cdiv(int64_t a, int64_t b) { return (a + b - 
 hipError_t launch_router_logits_simt(bool x_bf16, const void* x, const float* W_r, float* z,
                                      int64_t T, int d, int N, hipStream_t stream);
 
-// Router logits on MFMA: W_r split into three bf16 planes [N, 3d] (hi, mid, lo
-// residual parts whose sum is W_r exactly), x bf16.
-hipError_t launch_router_split_wr(const float* W_r, bf16_t* wr3, int d, int N, hipStream_t s);
-hipError_t launch_router_logits_mfma(const bf16_t* x, const bf16_t* wr3, float* z,
-                                     int64_t T, int d, int N, hipStream_t stream);
+// Router logits on MFMA for bf16 x: W_r split exactly into three bf16 parts
+// on the fly; K split into `nsplit` partial sums zpart[nsplit][T][N].
+int router_mfma_splits(int64_t T, int d, int N);
+hipError_t launch_router_logits_mfma(const bf16_t* x, const float* W_r, float* zpart, int64_t T,
+                                     int d, int N, int nsplit, hipStream_t stream);
 
-// Scores, group-limited top-k and gates from z.
-hipError_t launch_router_select(const float* z, const float* b, int64_t T, int N, int k,
+// Scores, group-limited top-k and gates from z (the sum of nsplit partials).
+hipError_t launch_router_select(const float* z, int nsplit, const float* b, int64_t T, int N, int k,
                                 int n_groups, int topk_groups, int group_topn, int gate,
                                 float route_scale, int32_t* idx, float* gates, float* scores,
                                 hipStream_t stream);
@@ -80,6 +80,8 @@ struct GroupedGemmArgs {
 // bf16 MFMA (act bf16, w bf16)
 hipError_t launch_gemm_bf16_swiglu(const GroupedGemmArgs& a, hipStream_t s);
 hipError_t launch_gemm_bf16_store(const GroupedGemmArgs& a, hipStream_t s);
+// second generation: 256x256 tiles, 8 wavefronts, direct-to-LDS 4-stage pipeline
+hipError_t launch_gemm_bf16_v2(const GroupedGemmArgs& a, bool swiglu, hipStream_t s);
 // fp32 SIMT (act f32, w f32)
 hipError_t launch_gemm_f32_swiglu(const GroupedGemmArgs& a, hipStream_t s);
 hipError_t launch_gemm_f32_store(const GroupedGemmArgs& a, hipStream_t s);

@@ -79,6 +79,174 @@ hipError_t launch_router_logits_simt(bool x_bf16, const void* x, const float* W_
 }
 
 // ---------------------------------------------------------------------------
+// z = x W_r on MFMA (x bf16).  W_r is fp32; every weight is split exactly into
+// three bf16 parts hi + mid + lo (successive round-to-nearest residuals: 8+8+8
+// significand bits cover fp32's 24), and each bf16 x bf16 product is exact in
+// the fp32 accumulator, so three v_mfma_f32_32x32x16_bf16 per fragment pair
+// give the fp32 dot product.  The split happens while the W_r tile is staged
+// into LDS.  128 tokens x 128 experts per 256-thread block, K staged 64 at a
+// time; blockIdx.z splits K (partial sums in zpart[z], added in split order by
+// the selection kernel) so that small token counts still fill the GPU.
+// ---------------------------------------------------------------------------
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2_t __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ uint32_t bf16_rne_bits(float f) {  // finite inputs
+  uint32_t u = __float_as_uint(f);
+  return (u + 0x7fffu + ((u >> 16) & 1u)) & 0xffff0000u;
+}
+
+__global__ __launch_bounds__(256, 1) void router_logits_mfma_kernel(
+    const bf16_t* __restrict__ x, const float* __restrict__ W, float* __restrict__ zpart,
+    int64_t T, int d, int N, int nsplit) {
+  constexpr int BM = 128, BN = 128, BK = 64;
+  __shared__ __attribute__((aligned(16))) bf16_t lds_a[2][BM * BK];
+  __shared__ __attribute__((aligned(16))) bf16_t lds_b[2][3][BN * BK];
+  const int tid = threadIdx.x;
+  const int64_t m0 = (int64_t)blockIdx.x * BM;
+  const int n0 = blockIdx.y * BN;
+  const int nk = d / BK;
+  const int kt0 = (int)((int64_t)blockIdx.z * nk / nsplit);
+  const int kt1 = (int)((int64_t)(blockIdx.z + 1) * nk / nsplit);
+
+  const bf16_t* a_src[4];
+  int a_lds[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int c = tid + 256 * i;
+    const int r = c >> 3, col = c & 7;
+    int64_t gr = m0 + r;
+    if (gr > T - 1) gr = T - 1;
+    a_src[i] = x + gr * d + col * 8;
+    a_lds[i] = r * BK + ((col ^ (r & 7)) << 3);
+  }
+  // W_r tile: 128 rows x 64 fp32 = 16 chunks of 16 B per row, 8 per thread
+  const float* b_src[8];
+  int b_lds[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int c = tid + 256 * i;
+    const int r = c >> 4, q = c & 15;  // q: 4-float group within the 64-wide K tile
+    int n = n0 + r;
+    if (n > N - 1) n = N - 1;
+    b_src[i] = W + (int64_t)n * d + q * 4;
+    const int c16 = q >> 1;
+    b_lds[i] = r * BK + ((c16 ^ (r & 7)) << 3) + (q & 1) * 4;
+  }
+  u32x4_t ra[4];
+  f32x4_t rb[8];
+#define RT_GLOAD(kt_)                                                        \
+  do {                                                                       \
+    const int ko_ = (kt_) * BK;                                              \
+    _Pragma("unroll") for (int i = 0; i < 4; ++i) ra[i] =                    \
+        *(const u32x4_t*)(a_src[i] + ko_);                                   \
+    _Pragma("unroll") for (int i = 0; i < 8; ++i) rb[i] =                    \
+        *(const f32x4_t*)(b_src[i] + ko_);                                   \
+  } while (0)
+#define RT_LSTORE(buf_)                                                      \
+  do {                                                                       \
+    _Pragma("unroll") for (int i = 0; i < 4; ++i)                            \
+        *(u32x4_t*)(&lds_a[(buf_)][a_lds[i]]) = ra[i];                       \
+    _Pragma("unroll") for (int i = 0; i < 8; ++i) {                          \
+      uint32_t h[4], m[4], l[4];                                             \
+      _Pragma("unroll") for (int e = 0; e < 4; ++e) {                        \
+        const float w = rb[i][e];                                            \
+        h[e] = bf16_rne_bits(w);                                             \
+        const float r1 = w - __uint_as_float(h[e]);                          \
+        m[e] = bf16_rne_bits(r1);                                            \
+        l[e] = bf16_rne_bits(r1 - __uint_as_float(m[e]));                    \
+      }                                                                      \
+      *(u32x2_t*)(&lds_b[(buf_)][0][b_lds[i]]) =                             \
+          u32x2_t{(h[0] >> 16) | h[1], (h[2] >> 16) | h[3]};                 \
+      *(u32x2_t*)(&lds_b[(buf_)][1][b_lds[i]]) =                             \
+          u32x2_t{(m[0] >> 16) | m[1], (m[2] >> 16) | m[3]};                 \
+      *(u32x2_t*)(&lds_b[(buf_)][2][b_lds[i]]) =                             \
+          u32x2_t{(l[0] >> 16) | l[1], (l[2] >> 16) | l[3]};                 \
+    }                                                                        \
+  } while (0)
+
+  const int lane = tid & 63, wv = tid >> 6;
+  const int wm = wv >> 1, wn = wv & 1;
+  const int l32 = lane & 31, khalf = lane >> 5;
+  f32x16_t acc[2][2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+
+  RT_GLOAD(kt0);
+  RT_LSTORE(0);
+  __syncthreads();
+  for (int kt = kt0; kt < kt1; ++kt) {
+    const int cur = (kt - kt0) & 1;
+    if (kt + 1 < kt1) RT_GLOAD(kt + 1);
+#pragma unroll
+    for (int ks = 0; ks < BK / 16; ++ks) {
+      const int chunk = 2 * ks + khalf;
+      bf16x8_t af[2], bfr[3][2];
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        const int r = wm * 64 + i * 32 + l32;
+        af[i] = *(const bf16x8_t*)(&lds_a[cur][r * BK + ((chunk ^ (r & 7)) << 3)]);
+      }
+#pragma unroll
+      for (int p = 0; p < 3; ++p)
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+          const int r = wn * 64 + j * 32 + l32;
+          bfr[p][j] = *(const bf16x8_t*)(&lds_b[cur][p][r * BK + ((chunk ^ (r & 7)) << 3)]);
+        }
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+#pragma unroll
+          for (int p = 0; p < 3; ++p)
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[p][j], acc[i][j], 0, 0, 0);
+    }
+    if (kt + 1 < kt1) RT_LSTORE(cur ^ 1);
+    __syncthreads();
+  }
+#undef RT_GLOAD
+#undef RT_LSTORE
+  float* __restrict__ zp = zpart + (int64_t)blockIdx.z * T * N;
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int64_t row = m0 + wm * 64 + i * 32 + 8 * (r >> 2) + 4 * khalf + (r & 3);
+      if (row >= T) continue;
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const int col = n0 + wn * 64 + j * 32 + l32;
+        if (col < N) zp[row * N + col] = acc[i][j][r];
+      }
+    }
+}
+
+int router_mfma_splits(int64_t T, int d, int N) {
+  const int64_t tiles = cdiv(T, 128) * cdiv(N, 128);
+  if (tiles <= 0) return 1;
+  const int nk = d / 64;
+  int64_t s = cdiv(512, tiles);
+  if (s > nk / 2) s = nk / 2;
+  if (s < 1) s = 1;
+  return (int)s;
+}
+
+hipError_t launch_router_logits_mfma(const bf16_t* x, const float* W_r, float* zpart, int64_t T,
+                                     int d, int N, int nsplit, hipStream_t stream) {
+  dim3 grid((unsigned)cdiv(T, 128), (unsigned)cdiv(N, 128), (unsigned)nsplit);
+  router_logits_mfma_kernel<<<grid, 256, 0, stream>>>(x, W_r, zpart, T, d, N, nsplit);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
 // Selection: one wavefront per token.  Lane l holds experts l, l+64, l+128,
 // l+192 (N <= 256).  Keys are compared as (ordered key << 32 | ~index), so a
 // 64-bit max picks the larger key and, on equal keys, the lower index.
@@ -93,7 +261,7 @@ __device__ __forceinline__ int unpack_idx(uint64_t p) {
 }
 
 __global__ __launch_bounds__(256) void router_select_kernel(
-    const float* __restrict__ z, const float* __restrict__ b, int64_t T, int N, int k,
+    const float* __restrict__ z, int nsplit, const float* __restrict__ b, int64_t T, int N, int k,
     int n_groups, int topk_groups, int group_topn, int gate, float route_scale,
     int32_t* __restrict__ out_idx, float* __restrict__ out_gate, float* __restrict__ scores) {
   const int lane = lane_id();
@@ -107,7 +275,9 @@ __global__ __launch_bounds__(256) void router_select_kernel(
   for (int j = 0; j < kSelPerLane; ++j) {
     const int e = lane + 64 * j;
     ok[j] = e < N;
-    const float zz = ok[j] ? z[t * N + e] : 0.f;
+    float zz = 0.f;
+    if (ok[j])
+      for (int sp = 0; sp < nsplit; ++sp) zz += z[((int64_t)sp * T + t) * N + e];
     const float bb = (ok[j] && b) ? b[e] : 0.f;
     val[j] = zz + bb;  // softmax: biased logit; overwritten below for sigmoid
     key[j] = bb;
@@ -221,12 +391,12 @@ __global__ __launch_bounds__(256) void router_select_kernel(
   }
 }
 
-hipError_t launch_router_select(const float* z, const float* b, int64_t T, int N, int k,
+hipError_t launch_router_select(const float* z, int nsplit, const float* b, int64_t T, int N, int k,
                                 int n_groups, int topk_groups, int group_topn, int gate,
                                 float route_scale, int32_t* idx, float* gates, float* scores,
                                 hipStream_t stream) {
   const unsigned blocks = (unsigned)cdiv(T, 4);
-  router_select_kernel<<<blocks, 256, 0, stream>>>(z, b, T, N, k, n_groups, topk_groups,
+  router_select_kernel<<<blocks, 256, 0, stream>>>(z, nsplit, b, T, N, k, n_groups, topk_groups,
                                                    group_topn, gate, route_scale, idx, gates,
                                                    scores);
   return hipGetLastError();

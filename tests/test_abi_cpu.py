@@ -83,5 +83,9 @@ def test_null_pointers_and_small_workspace_rejected(m):
 def test_empty_batch_is_a_no_op(m):
     c = m.config_from(datagen.get_config("v3_prefill"))
     c.T = 0
+    assert m.workspace_size(c) > 0
+    c.T, c.d = 1, 128
+    assert m.workspace_size(c) > 0
+    c.T, c.d = 0, 7168
     assert m._lib.LIB.moe_router(c, None, None, None, None, None, None, None, 0, None) == 0
     assert m._lib.LIB.moe_combine(c, None, None, None, None, None, None, None) == 0

@@ -156,7 +156,7 @@ def test_expert_ffn_ragged_groups(lib, wdt):
     say(f"   rel err {err:.3e} (bf16 output rounding alone: {floor:.3e})")
     assert err < tol_for(cfg)
     # beyond the output rounding, only the bf16 rounding of h and fp32 sums
-    assert err <= floor + (5e-3 if cfg.act_dtype == "bf16" else 2e-5)
+    assert err <= floor + (1e-2 if cfg.act_dtype == "bf16" else 2e-5)
 
 
 # ---------------------------------------------------------------- combine
@@ -187,10 +187,11 @@ def test_combine(lib, act, out):
     if out == "f32":
         assert rel_err(o.double().cpu().numpy(), ref) < 1e-6
         assert rel_err(o2.double().cpu().numpy(), delta) < 1e-6
-    else:  # one rounding of the fp32 sum: within half a bf16 ulp (+ fp32 slack)
-        for got, want in ((o, ref), (o2, delta)):
-            g = got.double().cpu().numpy()
-            assert np.all(np.abs(g - want) <= bf16_half_ulp(want) + 1e-5 * np.abs(want) + 1e-30)
+    else:  # one rounding of the fp32 sum: within half a bf16 ulp (+ fp32 sum slack)
+        mag = np.einsum("tk,tkd->td", np.abs(g), np.abs(yp[sr]))
+        for got, want, m in ((o, ref, mag + np.abs(ref - delta) * 2), (o2, delta, mag)):
+            gg = got.double().cpu().numpy()
+            assert np.all(np.abs(gg - want) <= bf16_half_ulp(want) + 1e-6 * m + 1e-30)
 
 
 # ---------------------------------------------------------------- forward
