@@ -74,14 +74,23 @@ def source_digest(*names) -> str:
     return h.hexdigest()[:16]
 
 
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "routed_up_gemm_v3_prefill_v3_decode_pmc_traffic.txt")
+COPY_CAL_BYTES = 256 << 20  # the calibration copy reads and writes this many bytes
+
+
+def read_traffic_db():
+    """The JSON object in the PMC traffic summary (lines after the '#' header)."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return {}
+    with open(TRAFFIC_FILE) as f:
+        body = "".join(l for l in f if not l.startswith("#"))
+    return json.loads(body) if body.strip() else {}
+
+
 def traffic_from_profile(kernel_key: str, sources, algorithmic_per_launch):
     """HBM bytes per launch from the committed PMC summary, or None when the
     kernel's sources changed since the counters were taken."""
-    path = os.path.join(ROOT, "profiles", "pmc_traffic.json")
-    if not os.path.exists(path):
-        return None
-    with open(path) as f:
-        db = json.load(f)
+    db = read_traffic_db()
     ent = db.get(kernel_key)
     if not ent or ent.get("source_digest") != source_digest(*sources):
         return None
@@ -154,11 +163,11 @@ def prefill_roofline(r):
     flops = 2.0 * cfg.T * cfg.k * cfg.d * 2 * cfg.inter  # W1 and W3 over all T*k routed rows
     ms = r["stage_ms"]["up"]
     achieved = flops / (ms * 1e-3) / 1e12
-    return {"bound": "mfma", "kernel": "gemm_bf16_grouped_kernel<SwiGLU> (routed W1|W3 + SwiGLU)",
+    return {"bound": "mfma", "kernel": "v2::gemm_bf16_v2_kernel<true, 8, 2, 64, 2> (routed W1|W3 + SwiGLU)",
             "achieved": round(achieved, 1), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
             "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
             "algorithmic_per_launch": flops, "avg_launch_ms": round(ms, 4),
-            "traffic": traffic_from_profile("prefill_up", ["gemm_bf16.hip", "grouped_sched.h"], flops)}
+            "traffic": traffic_from_profile("prefill_up", ["gemm_bf16_v2.hip", "grouped_sched.h"], flops)}
 
 
 def decode_summary(r):
@@ -224,7 +233,8 @@ def summarize_trace(path, title=""):
     agg = collections.defaultdict(list)
     for r in rows:
         dur = int(r["End_Timestamp"]) - int(r["Start_Timestamp"])
-        agg[(r["Kernel_Name"], r.get("Grid_Size", ""))].append(dur)
+        grid = r.get("Grid_Size") or r.get("Grid_Size_X", "")
+        agg[(r["Kernel_Name"], grid)].append(dur)
     total = sum(sum(v) for v in agg.values()) or 1
     if title:
         print(title)
@@ -234,9 +244,78 @@ def summarize_trace(path, title=""):
               f"{sum(v) / 1e6:10.3f} {100 * sum(v) / total:6.2f}")
 
 
+def copy_calibration():
+    """A plain elementwise copy of known size (reads and writes COPY_CAL_BYTES),
+    launched three times so that the FETCH_SIZE / WRITE_SIZE counters of the
+    same profiled process can be scaled to bytes."""
+    import torch
+    src = torch.ones(COPY_CAL_BYTES // 4, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        torch.mul(src, 1.0, out=dst)
+    torch.cuda.synchronize()
+    del src, dst
+
+
+def summarize_pmc(fetch_csv, write_csv, command):
+    """Per-launch HBM traffic of the routed W1|W3 GEMMs from two rocprofv3
+    --pmc runs of the same bench command (FETCH_SIZE, then WRITE_SIZE, KiB per
+    dispatch), each scaled by what the counter reads for the calibration copy.
+    Writes the traffic summary under profiles/ and prints it."""
+    import collections
+    import csv
+
+    def per_kernel(path, counter):
+        agg = collections.defaultdict(list)
+        for r in csv.DictReader(open(path)):
+            if r["Counter_Name"] != counter:
+                continue
+            agg[(r["Kernel_Name"], int(r["Grid_Size"]))].append(float(r["Counter_Value"]) * 1024.0)
+        return {k: sum(v) / len(v) for k, v in agg.items()}
+
+    fetch = per_kernel(fetch_csv, "FETCH_SIZE")
+    write = per_kernel(write_csv, "WRITE_SIZE")
+
+    def pick(table, pred):
+        keys = [k for k in table if pred(k[0])]
+        return max(keys, key=lambda k: k[1]) if keys else None  # largest grid = routed launch
+
+    cal_f = pick(fetch, lambda n: "MulFunctor" in n)
+    cal_w = pick(write, lambda n: "MulFunctor" in n)
+    sf = COPY_CAL_BYTES / fetch[cal_f]
+    sw = COPY_CAL_BYTES / write[cal_w]
+    db = {"calibration": {"copy_bytes": COPY_CAL_BYTES, "fetch_counter_bytes": fetch[cal_f],
+                          "write_counter_bytes": write[cal_w], "fetch_scale": sf, "write_scale": sw}}
+    targets = {
+        "prefill_up": (lambda n: "gemm_bf16_v2_kernel<true" in n, ["gemm_bf16_v2.hip", "grouped_sched.h"]),
+        "decode_up": (lambda n: "gemm_fp8_small_kernel<true" in n, ["gemm_fp8.hip", "grouped_sched.h"]),
+    }
+    for key, (pred, sources) in targets.items():
+        kf, kw = pick(fetch, pred), pick(write, pred)
+        if kf is None or kw is None:
+            continue
+        fb, wb = fetch[kf] * sf, write[kw] * sw
+        db[key] = {"kernel": kf[0], "grid": kf[1], "fetch_bytes": round(fb), "write_bytes": round(wb),
+                   "hbm_bytes_per_launch": round(fb + wb), "source_digest": source_digest(*sources)}
+    header = ("# HBM traffic per launch of the routed W1|W3 GEMMs (rocprofv3 --pmc, two runs)\n"
+              f"# command (run from /tmp, TMPDIR=/tmp), once with FETCH_SIZE and once with WRITE_SIZE:\n"
+              f"#   {command}\n"
+              "# each counter is scaled by its reading for a plain fp32 copy of "
+              f"{COPY_CAL_BYTES >> 20} MiB read + {COPY_CAL_BYTES >> 20} MiB written\n"
+              "# prefill_up = V3-shaped prefill (T=16384) routed up launch, decode_up = fp8 decode "
+              "(T=64) routed up launch; source_digest pins the kernel sources\n")
+    with open(TRAFFIC_FILE, "w") as f:
+        f.write(header)
+        f.write(json.dumps(db, indent=1) + "\n")
+    print(header + json.dumps(db, indent=1))
+
+
 def main():
     if len(sys.argv) > 1 and sys.argv[1] == "--summarize-trace":
         summarize_trace(sys.argv[2], sys.argv[3] if len(sys.argv) > 3 else "")
+        return
+    if len(sys.argv) > 1 and sys.argv[1] == "--summarize-pmc":
+        summarize_pmc(sys.argv[2], sys.argv[3], sys.argv[4] if len(sys.argv) > 4 else "")
         return
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -245,6 +324,8 @@ def main():
     ap.add_argument("--workload", default="v3_prefill")
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="launch a known-size copy first (scale for PMC byte counters)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (the layer is built and measured on a single "
@@ -254,6 +335,8 @@ def main():
     import torch
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     events = HipEvents()
+    if args.copy_calibration:
+        copy_calibration()
     r = run_workload(args.workload, args.steps, args.warmup, events)
     cfg = r["cfg"]
     value = cfg.T * args.steps / r["elapsed"]

@@ -6,13 +6,12 @@
 // columns side by side in LDS, SwiGLU in the epilogue, A rows optionally
 // gathered through row_index); down: Y = H W2^T.
 //
-// Workgroup: 512 threads = 8 wavefronts, 2 per SIMD.  Tile: 256 rows x 256
-// MFMA output columns (up: 128 columns of g and the same 128 of u).  Wave w
-// owns rows 128*(w/4) .. +128 and columns 64*(w%4) .. +64: 4 x 2 tiles of
-// v_mfma_f32_32x32x16_bf16, 128 fp32 accumulators.  The two waves sharing a
-// SIMD own the two row halves, and a wave skips its 32-row blocks that lie
-// past the expert's rows, so a tail tile costs each SIMD in proportion to
-// its valid rows; while one wave waits for LDS the other issues MFMAs.
+// Workgroup tile: 256 rows x 256 MFMA output columns (up: 128 columns of g
+// and the same 128 of u).  NWAVE wavefronts form a WGM x (NWAVE/WGM) grid;
+// each owns (256/WGM) rows x (256*WGM/NWAVE) columns as 32x32 tiles of
+// v_mfma_f32_32x32x16_bf16.  A wave skips its 32-row blocks that lie past
+// the expert's rows, so a tail tile costs in proportion to its valid rows
+// (the waves of one SIMD own different row ranges when NWAVE = 8).
 //
 // K is staged BK at a time through NS LDS stages filled by direct
 // global->LDS loads (global_load_lds_dwordx4) issued NS-1 k-tiles ahead; each
@@ -31,12 +30,16 @@ typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 typedef __attribute__((address_space(3))) void lds_void;
 
-constexpr int NTHR = 512, NWAVE = 8;
 constexpr int BM = 256, BN = 256;
-constexpr int WB = 4;  // 32-row blocks per wave
 
-template <int BK>
+template <int NWAVE, int WGM, int BK>
 struct Geom {
+  static constexpr int NTHR = NWAVE * 64;
+  static constexpr int WGN = NWAVE / WGM;                     // waves along N
+  static constexpr int WROWS = BM / WGM;                      // rows per wave
+  static constexpr int WCOLS = BN / WGN;                      // MFMA columns per wave
+  static constexpr int MB = WROWS / 32;                       // 32-row blocks per wave
+  static constexpr int NT = WCOLS / 32;                       // 32-column tiles per wave
   static constexpr int ROW_BYTES = BK * 2;
   static constexpr int CPR = BK / 8;                          // 16-byte chunks per row
   static constexpr int A_BYTES = BM * ROW_BYTES;
@@ -44,10 +47,19 @@ struct Geom {
   static constexpr int LOADS = STAGE_BYTES / (NTHR * 16);    // 16-byte loads per thread per stage
   static constexpr int ROWS_PER_KB = 1024 / ROW_BYTES;       // rows per 1 KiB load block
   static constexpr int ROWS_PER_256 = 256 / ROW_BYTES;       // rows per 256 B of LDS
+  static_assert(NT % 2 == 0, "the SwiGLU split needs an even number of column tiles");
   // A ds_read_b128 is served 16 lanes (256 B, all 64 banks) at a time; the 16
   // consecutive rows a lane group reads then land on 16 distinct bank slots.
   static __device__ __forceinline__ int swz(int row, int chunk) {
     return chunk ^ ((row / ROWS_PER_256) & (CPR - 1));
+  }
+  // LDS row of column tile j of wave column wn.  Up: the first NT/2 tiles are
+  // W1 rows, the last NT/2 the W3 rows of the same output columns.
+  template <bool SWIGLU>
+  static __device__ __forceinline__ int brow(int wn, int j) {
+    if (SWIGLU)
+      return (j < NT / 2 ? 0 : 128) + wn * (WCOLS / 2) + (j % (NT / 2)) * 32;
+    return wn * WCOLS + j * 32;
   }
 };
 
@@ -74,64 +86,24 @@ __device__ __forceinline__ void wait_ktile(int later) {
     wait_ktile_exact<LOADS, NS - 3>(later);
 }
 
-template <int NB>
-struct Frags {
-  bf16x8_t a[NB > 0 ? NB : 1];
-  bf16x8_t b[2];
-};
-
-template <bool SWIGLU, int NB, int BK>
-__device__ __forceinline__ void load_frags(const char* stage, int ks, int wm, int wn, int lane,
-                                           Frags<NB>& f) {
-  using G = Geom<BK>;
-  const int l32 = lane & 31, kh = lane >> 5;
-  const int chunk = 2 * ks + kh;
-#pragma unroll
-  for (int j = 0; j < 2; ++j) {
-    const int r = (SWIGLU ? j * 128 + wn * 32 : wn * 64 + j * 32) + l32;
-    f.b[j] = *(const bf16x8_t*)(stage + G::A_BYTES + r * G::ROW_BYTES + (G::swz(r, chunk) << 4));
-  }
-#pragma unroll
-  for (int i = 0; i < NB; ++i) {
-    const int r = wm * 128 + i * 32 + l32;
-    f.a[i] = *(const bf16x8_t*)(stage + r * G::ROW_BYTES + (G::swz(r, chunk) << 4));
-  }
-}
-
-template <int NB>
-__device__ __forceinline__ void mma(const Frags<NB>& f, f32x16_t (&acc)[WB][2]) {
-#pragma unroll
-  for (int i = 0; i < NB; ++i)
-#pragma unroll
-    for (int j = 0; j < 2; ++j)
-      acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.a[i], f.b[j], acc[i][j], 0, 0, 0);
-}
-
-// The K loop of one wavefront that owns NB valid 32-row blocks (0..4).  Every
+// The K loop of one wavefront that owns NB valid 32-row blocks.  Every
 // wavefront runs the same loads and barriers whatever its NB.
-//   SPREAD: the refill loads of a k-tile are issued a few at a time after each
-//   k-step's MFMAs instead of all at once after the barrier, so the 8
-//   wavefronts do not queue on the CU's address unit together.
-template <bool SWIGLU, int NB, int BK, int NS, bool SPREAD>
-__device__ __forceinline__ void kloop(int nk, const bf16_t* const (&src)[Geom<BK>::LOADS],
-                                      char (*lds)[Geom<BK>::STAGE_BYTES], int wm, int wn, int wv,
-                                      int lane, f32x16_t (&acc)[WB][2]) {
-  using G = Geom<BK>;
+template <bool SWIGLU, int NWAVE, int WGM, int BK, int NS, int NB>
+__device__ __forceinline__ void kloop(
+    int nk, const bf16_t* const (&src)[Geom<NWAVE, WGM, BK>::LOADS],
+    char (*lds)[Geom<NWAVE, WGM, BK>::STAGE_BYTES], int wm, int wn, int wv, int lane,
+    f32x16_t (&acc)[Geom<NWAVE, WGM, BK>::MB][Geom<NWAVE, WGM, BK>::NT]) {
+  using G = Geom<NWAVE, WGM, BK>;
   constexpr int LOADS = G::LOADS;
-  constexpr int KS = BK / 16;                // k-steps per k-tile
-  constexpr int LPK = LOADS / KS;            // loads issued after each k-step
-  static_assert(LOADS % KS == 0, "loads per k-step");
-#define V2_LOAD(kt_, st_, j_)                                                         \
-  __builtin_amdgcn_global_load_lds((const void*)(src[(j_)] + (kt_) * BK),            \
-                                   (lds_void*)(&lds[(st_)][(NWAVE * (j_) + wv) * 1024]), \
-                                   16, 0, 0)
 #pragma unroll
   for (int s = 0; s < NS - 1; ++s)
     if (s < nk) {
 #pragma unroll
-      for (int j = 0; j < LOADS; ++j) V2_LOAD(s, s, j);
+      for (int j = 0; j < LOADS; ++j)
+        __builtin_amdgcn_global_load_lds((const void*)(src[j] + s * BK),
+                                         (lds_void*)(&lds[s][(NWAVE * j + wv) * 1024]), 16, 0, 0);
     }
-  Frags<NB> f;
+  const int l32 = lane & 31, kh = lane >> 5;
   for (int kt = 0; kt < nk; ++kt) {
     // this thread's loads of k-tile kt are done once at most the loads of
     // the (up to NS-2) k-tiles after it are in flight
@@ -139,61 +111,80 @@ __device__ __forceinline__ void kloop(int nk, const bf16_t* const (&src)[Geom<BK
     // every thread's loads of kt have landed, and every wavefront has
     // finished reading the stage of k-tile kt-1, which is refilled next
     __builtin_amdgcn_s_barrier();
-    const bool refill = kt + NS - 1 < nk;
-    const int rst = (kt + NS - 1) % NS;
-    if (!SPREAD && refill) {
+    if (kt + NS - 1 < nk) {
+      const int st = (kt + NS - 1) % NS;
 #pragma unroll
-      for (int j = 0; j < LOADS; ++j) V2_LOAD(kt + NS - 1, rst, j);
+      for (int j = 0; j < LOADS; ++j)
+        __builtin_amdgcn_global_load_lds((const void*)(src[j] + (kt + NS - 1) * BK),
+                                         (lds_void*)(&lds[st][(NWAVE * j + wv) * 1024]), 16, 0, 0);
     }
     const char* stage = lds[kt % NS];
+    if (NB > 0) {
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      if (NB > 0) {
-        load_frags<SWIGLU, NB, BK>(stage, ks, wm, wn, lane, f);
-        mma<NB>(f, acc);
-      }
-      if (SPREAD) {
-        __builtin_amdgcn_sched_barrier(0);
-        if (refill) {
+      for (int ks = 0; ks < BK / 16; ++ks) {
+        const int chunk = 2 * ks + kh;
+        bf16x8_t b[G::NT], a[NB > 0 ? NB : 1];
 #pragma unroll
-          for (int j = ks * LPK; j < (ks + 1) * LPK; ++j) V2_LOAD(kt + NS - 1, rst, j);
+        for (int j = 0; j < G::NT; ++j) {
+          const int r = G::template brow<SWIGLU>(wn, j) + l32;
+          b[j] = *(const bf16x8_t*)(stage + G::A_BYTES + r * G::ROW_BYTES + (G::swz(r, chunk) << 4));
         }
-        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int i = 0; i < NB; ++i) {
+          const int r = wm * G::WROWS + i * 32 + l32;
+          a[i] = *(const bf16x8_t*)(stage + r * G::ROW_BYTES + (G::swz(r, chunk) << 4));
+        }
+#pragma unroll
+        for (int i = 0; i < NB; ++i)
+#pragma unroll
+          for (int j = 0; j < G::NT; ++j)
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
       }
     }
   }
-#undef V2_LOAD
 }
 
-template <bool SWIGLU, int BK, int NS, bool SPREAD>
-__global__ __launch_bounds__(NTHR, 1) void gemm_bf16_v2_kernel(GroupedGemmArgs args) {
-  using G = Geom<BK>;
+// Dispatches the K loop on the wave's number of valid row blocks (0..MB).
+template <bool SWIGLU, int NWAVE, int WGM, int BK, int NS, int NB>
+__device__ __forceinline__ void kloop_dispatch(
+    int nbw, int nk, const bf16_t* const (&src)[Geom<NWAVE, WGM, BK>::LOADS],
+    char (*lds)[Geom<NWAVE, WGM, BK>::STAGE_BYTES], int wm, int wn, int wv, int lane,
+    f32x16_t (&acc)[Geom<NWAVE, WGM, BK>::MB][Geom<NWAVE, WGM, BK>::NT]) {
+  if (nbw == NB || NB == 0)
+    kloop<SWIGLU, NWAVE, WGM, BK, NS, NB>(nk, src, lds, wm, wn, wv, lane, acc);
+  else if constexpr (NB > 0)
+    kloop_dispatch<SWIGLU, NWAVE, WGM, BK, NS, NB - 1>(nbw, nk, src, lds, wm, wn, wv, lane, acc);
+}
+
+template <bool SWIGLU, int NWAVE, int WGM, int BK, int NS>
+__global__ __launch_bounds__(NWAVE * 64, 1) void gemm_bf16_v2_kernel(GroupedGemmArgs args) {
+  using G = Geom<NWAVE, WGM, BK>;
   constexpr int LOADS = G::LOADS;
   // The tile lookup's scratch lives in the last stage, which is first
   // refilled after the first barrier of the K loop.
   __shared__ __attribute__((aligned(1024))) char lds[NS][G::STAGE_BYTES];
   int* s_ts = (int*)lds[NS - 1];
   int* s_scratch = s_ts + kMaxGroups + 8;
-  int* s_info = s_scratch + NTHR / 64;
+  int* s_info = s_scratch + G::NTHR / 64;
 
   // output columns per tile in the C matrix: up tiles cover 128 columns of H
   constexpr int CN = SWIGLU ? BN / 2 : BN;
   TileCoord tc;
-  if (!grouped_tile_lookup<NTHR>(args.offsets, args.n_groups, BM, CN, args.Nout, s_ts, s_scratch,
-                                 s_info, &tc))
+  if (!grouped_tile_lookup<G::NTHR>(args.offsets, args.n_groups, BM, CN, args.Nout, s_ts,
+                                    s_scratch, s_info, &tc))
     return;
 
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
-  const int wm = wv >> 2, wn = wv & 3;
+  const int wm = wv / G::WGN, wn = wv % G::WGN;
   const int K = args.K, Nout = args.Nout;
   const int64_t nrows64 = tc.rend - tc.row0;
   const int nrows = nrows64 < BM ? (int)nrows64 : BM;
   const int nblk = (nrows + 31) >> 5;
-  int nbw = nblk - WB * wm;
-  nbw = nbw < 0 ? 0 : (nbw > WB ? WB : nbw);
+  int nbw = nblk - G::MB * wm;
+  nbw = nbw < 0 ? 0 : (nbw > G::MB ? G::MB : nbw);
 
   // per-thread sources of the direct loads of a stage; instruction j of
-  // wavefront wv fills the 1 KiB LDS block 8*j + wv
+  // wavefront wv fills the 1 KiB LDS block NWAVE*j + wv
   const bf16_t* src[LOADS];
 #pragma unroll
   for (int j = 0; j < LOADS; ++j) {
@@ -221,43 +212,39 @@ __global__ __launch_bounds__(NTHR, 1) void gemm_bf16_v2_kernel(GroupedGemmArgs a
     }
   }
 
-  f32x16_t acc[WB][2];
+  f32x16_t acc[G::MB][G::NT];
 #pragma unroll
-  for (int i = 0; i < WB; ++i)
+  for (int i = 0; i < G::MB; ++i)
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
+    for (int j = 0; j < G::NT; ++j)
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
-  const int nk = K / BK;
-  switch (nbw) {
-    case 4: kloop<SWIGLU, 4, BK, NS, SPREAD>(nk, src, lds, wm, wn, wv, lane, acc); break;
-    case 3: kloop<SWIGLU, 3, BK, NS, SPREAD>(nk, src, lds, wm, wn, wv, lane, acc); break;
-    case 2: kloop<SWIGLU, 2, BK, NS, SPREAD>(nk, src, lds, wm, wn, wv, lane, acc); break;
-    case 1: kloop<SWIGLU, 1, BK, NS, SPREAD>(nk, src, lds, wm, wn, wv, lane, acc); break;
-    default: kloop<SWIGLU, 0, BK, NS, SPREAD>(nk, src, lds, wm, wn, wv, lane, acc); break;
-  }
+  kloop_dispatch<SWIGLU, NWAVE, WGM, BK, NS, G::MB>(nbw, K / BK, src, lds, wm, wn, wv, lane, acc);
 
   bf16_t* __restrict__ C = (bf16_t*)args.C;
   const int l32 = lane & 31, kh = lane >> 5;
 #pragma unroll
-  for (int i = 0; i < WB; ++i) {
+  for (int i = 0; i < G::MB; ++i) {
     if (i >= nbw) break;
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
-      const int row = wm * 128 + i * 32 + 8 * (r >> 2) + 4 * kh + (r & 3);
+      const int row = wm * G::WROWS + i * 32 + 8 * (r >> 2) + 4 * kh + (r & 3);
       if (row >= nrows) continue;
       bf16_t* crow = C + (tc.row0 + row) * Nout;
       if (SWIGLU) {
-        const int col = tc.n0 + wn * 32 + l32;
-        if (col < Nout) {
-          const float g = acc[i][0][r], u = acc[i][1][r];
-          crow[col] = f32_to_bf16(g / (1.f + __expf(-g)) * u);
+#pragma unroll
+        for (int j = 0; j < G::NT / 2; ++j) {
+          const int col = tc.n0 + wn * (G::WCOLS / 2) + j * 32 + l32;
+          if (col < Nout) {
+            const float g = acc[i][j][r], u = acc[i][j + G::NT / 2][r];
+            crow[col] = f32_to_bf16(g / (1.f + __expf(-g)) * u);
+          }
         }
       } else {
 #pragma unroll
-        for (int j = 0; j < 2; ++j) {
-          const int col = tc.n0 + wn * 64 + j * 32 + l32;
+        for (int j = 0; j < G::NT; ++j) {
+          const int col = tc.n0 + wn * G::WCOLS + j * 32 + l32;
           if (col < Nout) crow[col] = f32_to_bf16(acc[i][j][r]);
         }
       }
@@ -266,8 +253,7 @@ __global__ __launch_bounds__(NTHR, 1) void gemm_bf16_v2_kernel(GroupedGemmArgs a
 }
 
 // Configuration used by the library (K must be a multiple of BK).
-constexpr int LIB_BK = 64, LIB_NS = 2;
-constexpr bool LIB_SPREAD = false;
+constexpr int LIB_NWAVE = 8, LIB_WGM = 2, LIB_BK = 64, LIB_NS = 2;
 
 }  // namespace v2
 
@@ -275,10 +261,13 @@ hipError_t launch_gemm_bf16_v2(const GroupedGemmArgs& a, bool swiglu, hipStream_
   const int cn = swiglu ? v2::BN / 2 : v2::BN;
   const int64_t grid = grouped_grid(a.max_rows, a.n_groups, v2::BM, cn, a.Nout);
   if (grid <= 0) return hipSuccess;
+  constexpr int nthr = v2::LIB_NWAVE * 64;
   if (swiglu)
-    v2::gemm_bf16_v2_kernel<true, v2::LIB_BK, v2::LIB_NS, v2::LIB_SPREAD><<<(unsigned)grid, v2::NTHR, 0, s>>>(a);
+    v2::gemm_bf16_v2_kernel<true, v2::LIB_NWAVE, v2::LIB_WGM, v2::LIB_BK, v2::LIB_NS>
+        <<<(unsigned)grid, nthr, 0, s>>>(a);
   else
-    v2::gemm_bf16_v2_kernel<false, v2::LIB_BK, v2::LIB_NS, v2::LIB_SPREAD><<<(unsigned)grid, v2::NTHR, 0, s>>>(a);
+    v2::gemm_bf16_v2_kernel<false, v2::LIB_NWAVE, v2::LIB_WGM, v2::LIB_BK, v2::LIB_NS>
+        <<<(unsigned)grid, nthr, 0, s>>>(a);
   return hipGetLastError();
 }
 

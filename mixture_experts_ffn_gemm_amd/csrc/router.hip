@@ -229,12 +229,16 @@ __global__ __launch_bounds__(256, 1) void router_logits_mfma_kernel(
     }
 }
 
+// Partial sums are added by the selection kernel, so the split stays small.
+constexpr int kRouterMaxSplits = 8;
+
 int router_mfma_splits(int64_t T, int d, int N) {
   const int64_t tiles = cdiv(T, 128) * cdiv(N, 128);
   if (tiles <= 0) return 1;
   const int nk = d / 64;
   int64_t s = cdiv(512, tiles);
   if (s > nk / 2) s = nk / 2;
+  if (s > kRouterMaxSplits) s = kRouterMaxSplits;
   if (s < 1) s = 1;
   return (int)s;
 }
@@ -276,8 +280,15 @@ __global__ __launch_bounds__(256) void router_select_kernel(
     const int e = lane + 64 * j;
     ok[j] = e < N;
     float zz = 0.f;
-    if (ok[j])
-      for (int sp = 0; sp < nsplit; ++sp) zz += z[((int64_t)sp * T + t) * N + e];
+    if (ok[j]) {
+      // load the (at most 8) split partials together, then add them in split order
+      float part[8];
+#pragma unroll
+      for (int sp = 0; sp < 8; ++sp) part[sp] = sp < nsplit ? z[((int64_t)sp * T + t) * N + e] : 0.f;
+#pragma unroll
+      for (int sp = 0; sp < 8; ++sp)
+        if (sp < nsplit) zz += part[sp];
+    }
     const float bb = (ok[j] && b) ? b[e] : 0.f;
     val[j] = zz + bb;  // softmax: biased logit; overwritten below for sigmoid
     key[j] = bb;
