@@ -163,11 +163,11 @@ def prefill_roofline(r):
     flops = 2.0 * cfg.T * cfg.k * cfg.d * 2 * cfg.inter  # W1 and W3 over all T*k routed rows
     ms = r["stage_ms"]["up"]
     achieved = flops / (ms * 1e-3) / 1e12
-    return {"bound": "mfma", "kernel": "v2::gemm_bf16_v2_kernel<true, 8, 2, 64, 2> (routed W1|W3 + SwiGLU)",
+    return {"bound": "mfma", "kernel": "gp::gemm_bf16_persist_kernel<32, 4, true> (routed W1|W3 + SwiGLU)",
             "achieved": round(achieved, 1), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
             "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
             "algorithmic_per_launch": flops, "avg_launch_ms": round(ms, 4),
-            "traffic": traffic_from_profile("prefill_up", ["gemm_bf16_v2.hip", "grouped_sched.h"], flops)}
+            "traffic": traffic_from_profile("prefill_up", ["gemm_bf16_persist.hip", "grouped_sched.h"], flops)}
 
 
 def decode_summary(r):
@@ -230,17 +230,20 @@ def summarize_trace(path, title=""):
     import collections
     import csv
     rows = list(csv.DictReader(open(path)))
+    # launches of one kernel with one grid but on different streams (a
+    # persistent grid serves the routed experts on the main stream and the
+    # shared expert on the side stream) are listed apart: grid/stream
     agg = collections.defaultdict(list)
     for r in rows:
         dur = int(r["End_Timestamp"]) - int(r["Start_Timestamp"])
         grid = r.get("Grid_Size") or r.get("Grid_Size_X", "")
-        agg[(r["Kernel_Name"], grid)].append(dur)
+        agg[(r["Kernel_Name"], f"{grid}/s{r.get('Stream_Id', '?')}")].append(dur)
     total = sum(sum(v) for v in agg.values()) or 1
     if title:
         print(title)
-    print(f"{'kernel':100s} {'grid':>9s} {'calls':>6s} {'avg_us':>10s} {'total_ms':>10s} {'pct':>6s}")
+    print(f"{'kernel':100s} {'grid/stream':>12s} {'calls':>6s} {'avg_us':>10s} {'total_ms':>10s} {'pct':>6s}")
     for (name, grid), v in sorted(agg.items(), key=lambda kv: -sum(kv[1])):
-        print(f"{name[:100]:100s} {grid:>9s} {len(v):6d} {sum(v) / len(v) / 1e3:10.2f} "
+        print(f"{name[:100]:100s} {grid:>12s} {len(v):6d} {sum(v) / len(v) / 1e3:10.2f} "
               f"{sum(v) / 1e6:10.3f} {100 * sum(v) / total:6.2f}")
 
 
@@ -266,12 +269,19 @@ def summarize_pmc(fetch_csv, write_csv, command):
     import csv
 
     def per_kernel(path, counter):
+        # the routed and the shared launches of one kernel share its name and
+        # (persistent) grid; the routed one moves several times more bytes, so
+        # each kernel's figure is the mean over its dispatches above half its max
         agg = collections.defaultdict(list)
         for r in csv.DictReader(open(path)):
             if r["Counter_Name"] != counter:
                 continue
             agg[(r["Kernel_Name"], int(r["Grid_Size"]))].append(float(r["Counter_Value"]) * 1024.0)
-        return {k: sum(v) / len(v) for k, v in agg.items()}
+        out = {}
+        for k, v in agg.items():
+            big = [x for x in v if x >= 0.5 * max(v)]
+            out[k] = sum(big) / len(big)
+        return out
 
     fetch = per_kernel(fetch_csv, "FETCH_SIZE")
     write = per_kernel(write_csv, "WRITE_SIZE")
@@ -287,7 +297,8 @@ def summarize_pmc(fetch_csv, write_csv, command):
     db = {"calibration": {"copy_bytes": COPY_CAL_BYTES, "fetch_counter_bytes": fetch[cal_f],
                           "write_counter_bytes": write[cal_w], "fetch_scale": sf, "write_scale": sw}}
     targets = {
-        "prefill_up": (lambda n: "gemm_bf16_v2_kernel<true" in n, ["gemm_bf16_v2.hip", "grouped_sched.h"]),
+        "prefill_up": (lambda n: "gemm_bf16_persist_kernel<32, 4, true>" in n,
+                       ["gemm_bf16_persist.hip", "grouped_sched.h"]),
         "decode_up": (lambda n: "gemm_fp8_small_kernel<true" in n, ["gemm_fp8.hip", "grouped_sched.h"]),
     }
     for key, (pred, sources) in targets.items():

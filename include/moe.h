@@ -174,8 +174,11 @@ int moe_combine(const moe_config* cfg, const void* y_perm, const int32_t* slot_r
 
 /*
  * moe_forward - the whole layer: router -> permute -> routed experts (fused
- * gather) -> combine, with the shared MLP on `stream_side` overlapping the
- * routed path (stream_side may equal stream_main or be NULL).
+ * gather) -> combine.  The shared MLP runs on `stream_side`, overlapping the
+ * routed path.  stream_side may be NULL or equal stream_main: then, with bf16
+ * weights and one shared expert (S = 1), the shared expert runs inside the
+ * routed grouped GEMMs as one more group whose rows are all T tokens (results
+ * are bitwise the same either way), and otherwise after the routed path.
  *   x [T, d];  W_r [N, d];  b [N] nullable
  *   W1, W3 [N, I, d];  W2 [N, d, I];  s1, s3, s2 fp8 scales or NULL
  *   W1s, W3s [S*I, d];  W2s [d, S*I];  s1s, s3s, s2s   (all NULL when S = 0)
@@ -192,7 +195,9 @@ int moe_forward(const moe_config* cfg, const void* x, const float* W_r, const fl
                 void* out, int32_t* topk_idx_out, float* topk_gate_out, int32_t* counts_out,
                 void* ws, size_t ws_bytes, void* stream_main, void* stream_side);
 
-/* Stages of moe_forward, in launch order (shared ones run on stream_side). */
+/* Stages of moe_forward, in launch order (shared ones run on stream_side;
+ * when the shared expert is folded into the routed GEMMs, UP and DOWN cover it
+ * and the two shared stages are empty intervals on stream_main). */
 typedef enum {
   MOE_STAGE_ROUTER = 0,      /* logits + selection                 (stream_main) */
   MOE_STAGE_PERMUTE = 1,     /* histogram, scan, scatter           (stream_main) */

@@ -35,6 +35,11 @@ struct Layout {
   int64_t h_elems;  // capacity of the h region in activation elements
 };
 
+// bf16 with one shared expert and no second stream to overlap it on: the
+// shared expert runs inside the routed grouped GEMMs as one more group (its
+// rows: every token, in order).  The workspace is sized for both ways.
+bool can_fold_shared(const moe_config& c) { return c.w_dtype == MOE_BF16 && c.n_shared == 1; }
+
 Layout make_layout(const moe_config& c) {
   Layout L{};
   size_t off = 0;
@@ -54,15 +59,17 @@ Layout make_layout(const moe_config& c) {
   L.hist = take(nchunks * N * 4);
   L.base = take(nchunks * N * 4);
   L.rank = take(slots * 4);
+  const bool fold = can_fold_shared(c);
+  const int64_t grp_rows = fold ? slots + T : slots;  // rows of the grouped GEMMs
   L.counts = take(N * 4);
-  L.offsets = take((N + 1) * 4);
-  L.row_token = take(slots * 4);
+  L.offsets = take((N + 2) * 4);
+  L.row_token = take(grp_rows * 4);
   L.slot_row = take(slots * 4);
-  const int64_t rows_max = slots > T ? slots : T;
+  const int64_t rows_max = grp_rows > T ? grp_rows : T;
   const int64_t inter_max = S * I > I ? S * I : I;
   L.h_elems = rows_max * inter_max;
   L.h = take(L.h_elems * as);
-  L.y = take(slots * d * as);
+  L.y = take(grp_rows * d * as);
   L.hs = take(T * S * I * as);
   L.ys = take(S > 0 ? T * d * as : 0);
   L.shoff = take(2 * 4);
@@ -148,8 +155,12 @@ int run_expert_ffn(const moe_config* c, int n_experts, const int32_t* offsets, i
                    int inter, const void* x_rows, const int32_t* row_index, const void* W1,
                    const void* W3, const void* W2, const float* s1, const float* s3,
                    const float* s2, void* h, void* y_rows, hipStream_t s,
-                   void* const* ev = nullptr, int stage_up = -1, int stage_dn = -1) {
+                   void* const* ev = nullptr, int stage_up = -1, int stage_dn = -1,
+                   const void* W1x = nullptr, const void* W3x = nullptr,
+                   const void* W2x = nullptr) {
   GroupedGemmArgs up{};
+  up.B0x = W1x;
+  up.B1x = W3x;
   up.A = x_rows;
   up.row_index = row_index;
   up.offsets = offsets;
@@ -163,6 +174,7 @@ int run_expert_ffn(const moe_config* c, int n_experts, const int32_t* offsets, i
   up.Nout = inter;
   up.K = c->d;
   GroupedGemmArgs dn{};
+  dn.B0x = W2x;
   dn.A = h;
   dn.row_index = nullptr;
   dn.offsets = offsets;
@@ -175,11 +187,19 @@ int run_expert_ffn(const moe_config* c, int n_experts, const int32_t* offsets, i
   dn.C = y_rows;
   dn.Nout = c->d;
   dn.K = inter;
+  // bf16: the persistent kernel takes K >= 128 (four 32-deep steps) and
+  // A byte offsets below 4 GiB; anything else goes to the 8-wave kernel
+  auto bf16_gemm = [&](const GroupedGemmArgs& a, bool swiglu, int64_t a_rows) {
+    if (a.K % 32 == 0 && a.K >= 128 && a_rows * (int64_t)a.K * 2 < (int64_t(1) << 32) - 4096)
+      return launch_gemm_bf16_persist(a, swiglu, s);
+    return launch_gemm_bf16_v2(a, swiglu, s);
+  };
+  const int64_t up_rows = row_index ? (c->T > max_rows ? c->T : max_rows) : max_rows;
   MOE_HIP_CHECK(mark(ev, stage_up, false, s));
   if (c->w_dtype == MOE_F32)
     MOE_HIP_CHECK(launch_gemm_f32_swiglu(up, s));
   else if (c->w_dtype == MOE_BF16)
-    MOE_HIP_CHECK(launch_gemm_bf16_v2(up, true, s));
+    MOE_HIP_CHECK(bf16_gemm(up, true, up_rows));
   else
     MOE_HIP_CHECK(launch_gemm_fp8_swiglu(up, s));
   MOE_HIP_CHECK(mark(ev, stage_up, true, s));
@@ -187,7 +207,7 @@ int run_expert_ffn(const moe_config* c, int n_experts, const int32_t* offsets, i
   if (c->w_dtype == MOE_F32)
     MOE_HIP_CHECK(launch_gemm_f32_store(dn, s));
   else if (c->w_dtype == MOE_BF16)
-    MOE_HIP_CHECK(launch_gemm_bf16_v2(dn, false, s));
+    MOE_HIP_CHECK(bf16_gemm(dn, false, max_rows));
   else
     MOE_HIP_CHECK(launch_gemm_fp8_store(dn, s));
   MOE_HIP_CHECK(mark(ev, stage_dn, true, s));
@@ -330,6 +350,7 @@ static int forward_impl(const moe_config* cfg, const void* x, const float* W_r, 
   const Layout L = make_layout(c);
   hipStream_t sm = (hipStream_t)stream_main;
   hipStream_t ss = stream_side ? (hipStream_t)stream_side : sm;
+  const bool fold = can_fold_shared(c) && ss == sm;
   const bool two_streams = ss != sm && c.n_shared > 0;
 
   struct Events {  // destroyed on every return path; pending events are released by HIP
@@ -348,7 +369,7 @@ static int forward_impl(const moe_config* cfg, const void* x, const float* W_r, 
     MOE_HIP_CHECK(hipStreamWaitEvent(ss, ev_fork, 0));
   }
   void* ys = nullptr;
-  if (c.n_shared > 0) {
+  if (c.n_shared > 0 && !fold) {
     // shared MLP of width S * I over every token (one expert, rows {0, T})
     int32_t* shoff = at<int32_t>(ws, L.shoff);
     ys = at<void>(ws, L.ys);
@@ -373,10 +394,26 @@ static int forward_impl(const moe_config* cfg, const void* x, const float* W_r, 
   MOE_HIP_CHECK(launch_permute(idx, c.T, c.k, c.n_routed, at<int32_t>(ws, L.hist),
                                at<int32_t>(ws, L.base), at<int32_t>(ws, L.rank), counts, offsets,
                                row_token, slot_row, sm));
+  const int64_t slots = c.T * c.k;
+  if (fold)
+    MOE_HIP_CHECK(launch_append_shared_rows(row_token + slots, (int32_t)c.T,
+                                            offsets + c.n_routed + 1, (int32_t)(slots + c.T), sm));
   MOE_HIP_CHECK(mark(ev, MOE_STAGE_PERMUTE, true, sm));
   void* y = at<void>(ws, L.y);
-  st = run_expert_ffn(cfg, c.n_routed, offsets, c.T * c.k, c.inter, x, row_token, W1, W3, W2, s1,
-                      s3, s2, at<void>(ws, L.h), y, sm, ev, MOE_STAGE_UP, MOE_STAGE_DOWN);
+  if (fold) {
+    // routed experts and the shared expert (group n_routed) in one launch each
+    st = run_expert_ffn(cfg, c.n_routed + 1, offsets, slots + c.T, c.inter, x, row_token, W1, W3,
+                        W2, s1, s3, s2, at<void>(ws, L.h), y, sm, ev, MOE_STAGE_UP,
+                        MOE_STAGE_DOWN, W1s, W3s, W2s);
+    ys = (char*)y + slots * c.d * act_bytes(c.act_dtype);
+    for (int stg : {MOE_STAGE_SHARED_UP, MOE_STAGE_SHARED_DOWN}) {  // folded: empty intervals
+      MOE_HIP_CHECK(mark(ev, stg, false, sm));
+      MOE_HIP_CHECK(mark(ev, stg, true, sm));
+    }
+  } else {
+    st = run_expert_ffn(cfg, c.n_routed, offsets, slots, c.inter, x, row_token, W1, W3, W2, s1,
+                        s3, s2, at<void>(ws, L.h), y, sm, ev, MOE_STAGE_UP, MOE_STAGE_DOWN);
+  }
   if (st) return st;
   if (two_streams) MOE_HIP_CHECK(hipStreamWaitEvent(sm, ev_join, 0));
   MOE_HIP_CHECK(mark(ev, MOE_STAGE_COMBINE, false, sm));

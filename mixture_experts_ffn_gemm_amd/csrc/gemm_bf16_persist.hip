@@ -1,0 +1,478 @@
+// Grouped bf16 expert GEMMs on gfx950 MFMA: persistent, one wavefront per
+// SIMD, with one software pipeline running across all tiles of a workgroup.
+//
+// Expert FFN (open-model-atlas, "DeepSeek-V3.2-Exp - Mixture of experts",
+// "All 19 steps", routed expert): g = x W1, u = x W3, h = silu(g) * u,
+// E = h W2.  Up: H = silu(A W1^T) * (A W3^T) (W1 and W3 tiles of the same
+// columns side by side in LDS, SwiGLU in the epilogue, A rows optionally
+// gathered through row_index); down: Y = H W2^T.
+//
+// Work split.  Output tiles are 256 rows x 256 MFMA columns (up: 128 columns
+// of g and the same 128 of u), enumerated expert-major, then N-tile, then
+// M-tile; experts with no rows own no tile and are never read.  The grid has
+// one workgroup per CU.  The tile list is cut into one contiguous range per
+// XCD, and the workgroups of an XCD take its tiles round-robin, so at any time
+// an XCD works on consecutive tiles that share weight panels and activation
+// rows through its L2.  Every workgroup rebuilds the per-expert tile prefix
+// from the device offsets in LDS; the host never waits for the counts.
+//
+// Workgroup: 256 threads = 4 wavefronts, one per SIMD.  Wave w owns the
+// 32-row blocks w/2, w/2+2, .. (interleaved, so a partly filled tile still
+// spreads its MFMAs over all four SIMDs) and columns 128*(w%2) .. +128 of the
+// tile, as 4 x 4 tiles of v_mfma_f32_32x32x16_bf16 with the weight fragment
+// as the first operand, so each lane accumulates 4 runs of 4 consecutive
+// output columns of one row (256 fp32 accumulators in the AGPRs).  A lane pair (l, l+32) trades halves
+// with v_permlane32_swap in the epilogue and each lane stores 16 bytes.
+//
+// Pipeline.  K is staged BK at a time through NS LDS stages by direct
+// global->LDS loads (global_load_lds_dwordx4).  A "step" is one BK slice of one
+// tile; the steps of all tiles of the workgroup form one sequence, and the
+// loads of step q+NS-1 are issued during step q, one or two at a time between
+// groups of four MFMAs, so the texture path sees an even stream instead of a
+// burst.  The fragments of the next k-step are read from LDS while the MFMAs of
+// the current one run.  One barrier per step, between the two halves of the
+// last k-step's MFMAs.  The gathered row indices of the tile after next are
+// fetched into LDS by a direct load too, so no load result is ever waited for
+// in registers.  LDS rows hold BK bf16 of one matrix row; their 16-byte chunks
+// are XOR-swizzled so the fragment reads are free of bank conflicts.  A wave
+// skips the MFMAs of its 32-row blocks past the expert's rows.
+#include "grouped_sched.h"
+#include "moe_internal.h"
+
+namespace moe {
+
+namespace gp {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+typedef unsigned u32x4_t __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef __attribute__((address_space(3))) void lds_void;
+
+constexpr int BM = 256, BN = 256, NTHR = 256, NWAVE = 4, MB = 4, NT = 4;
+
+template <int BK>
+struct Geo {
+  static constexpr int ROW_BYTES = BK * 2;
+  static constexpr int CPR = BK / 8;                      // 16-byte chunks per LDS row
+  static constexpr int A_BYTES = BM * ROW_BYTES;
+  static constexpr int STAGE_BYTES = (BM + BN) * ROW_BYTES;
+  static constexpr int LOADS = STAGE_BYTES / (NTHR * 16); // direct loads per thread per step
+  static constexpr int A_LOADS = A_BYTES / (NTHR * 16);
+  static constexpr int ROWS_PER_KB = 1024 / ROW_BYTES;
+  static constexpr int ROWS_PER_256 = 256 / ROW_BYTES;
+  static constexpr int KS = BK / 16;                      // k-steps per step
+  // A ds_read_b128 is served 16 lanes (256 B, all 64 banks) at a time; the
+  // 16 consecutive rows a lane group reads then land on 16 distinct slots.
+  static __device__ __forceinline__ int swz(int row, int chunk) {
+    return chunk ^ ((row / ROWS_PER_256) & (CPR - 1));
+  }
+};
+
+// LDS row of column tile j of wave column wn.  Up: tiles 0, 1 are W1 rows,
+// tiles 2, 3 the W3 rows of the same output columns.
+template <bool SWIGLU>
+__device__ __forceinline__ int brow(int wn, int j) {
+  if (SWIGLU) return (j < 2 ? 0 : 128) + wn * 64 + (j & 1) * 32;
+  return wn * 128 + j * 32;
+}
+
+// s_waitcnt on the vector-memory counter (gfx9 encoding), and on every LDS
+// access of this wavefront too.
+template <int N>
+__device__ __forceinline__ void wait_vm_lgkm() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4));
+}
+
+struct Frags {
+  bf16x8_t a[MB], b[NT];
+};
+
+template <int BK, bool SWIGLU>
+__device__ __forceinline__ void read_frags(const char* stage, int ks, int wm, int wn, int lane,
+                                           Frags& f) {
+  using G = Geo<BK>;
+  const int l32 = lane & 31, chunk = 2 * ks + (lane >> 5);
+#pragma unroll
+  for (int j = 0; j < NT; ++j) {
+    const int r = brow<SWIGLU>(wn, j) + l32;
+    f.b[j] = *(const bf16x8_t*)(stage + G::A_BYTES + r * G::ROW_BYTES + (G::swz(r, chunk) << 4));
+  }
+#pragma unroll
+  for (int i = 0; i < MB; ++i) {
+    const int r = (2 * i + wm) * 32 + l32;
+    f.a[i] = *(const bf16x8_t*)(stage + r * G::ROW_BYTES + (G::swz(r, chunk) << 4));
+  }
+}
+
+// The four MFMAs of row block i of one k-step (skipped past the wave's rows).
+template <int NB>
+__device__ __forceinline__ void mfma_row(int i, const Frags& f, f32x16_t (&acc)[MB][NT]) {
+  if (i < NB) {
+#pragma unroll
+    for (int j = 0; j < NT; ++j)
+      acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.b[j], f.a[i], acc[i][j], 0, 0, 0);
+  }
+}
+
+// Per-workgroup tile table in LDS.
+struct TileTab {
+  int ts[kMaxGroups + 1];   // exclusive prefix of M-tiles per group
+  int off[kMaxGroups + 1];  // row offsets of the groups
+  int scan[NTHR / 64];
+  int ri[2][BM];            // gathered row indices of upcoming tiles
+};
+
+struct Tile {
+  int g, n0;
+  int64_t row0, rend;
+};
+
+__device__ __forceinline__ Tile decode_tile(const TileTab& tt, int n_groups, int ntn, int CN,
+                                            int L) {
+  // the group g with ts[g]*ntn <= L < ts[g+1]*ntn (ts[0] = 0, ts[n] * ntn > L)
+  int lo = 0, hi = n_groups;
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if (tt.ts[mid] * ntn <= L) lo = mid;
+    else hi = mid;
+  }
+  const int tiles_g = tt.ts[lo + 1] - tt.ts[lo];
+  const int rem = L - tt.ts[lo] * ntn;
+  Tile t;
+  t.g = lo;
+  t.row0 = (int64_t)tt.off[lo] + (int64_t)(rem % tiles_g) * BM;
+  t.rend = tt.off[lo + 1];
+  t.n0 = (rem / tiles_g) * CN;
+  return t;
+}
+
+// The issue side of the pipeline: which step's slice the next direct loads
+// fetch, and their sources in the current tile: a wave-uniform base per load
+// and a 32-bit per-lane byte offset.
+template <int BK, bool SWIGLU>
+struct Issuer {
+  using G = Geo<BK>;
+  const char* base[G::LOADS];
+  unsigned off[G::LOADS];
+  int it, kt;  // tile index within this workgroup's list, step within the tile
+
+  __device__ __forceinline__ void build(const GroupedGemmArgs& a, const TileTab& tt,
+                                        const Tile& t, int wv, int lane) {
+    const int rib = lane / G::CPR, phys = lane % G::CPR;
+    const int64_t rowb = (int64_t)a.K * 2;  // bytes per matrix row
+#pragma unroll
+    for (int j = 0; j < G::LOADS; ++j) {
+      const int blk = NWAVE * j + wv;
+      if (j < G::A_LOADS) {
+        const int r = blk * G::ROWS_PER_KB + rib;
+        int64_t row;
+        if (a.row_index) {
+          row = tt.ri[it & 1][r];
+        } else {
+          row = t.row0 + r;
+          if (row > t.rend - 1) row = t.rend - 1;
+        }
+        base[j] = (const char*)a.A;
+        off[j] = (unsigned)(row * rowb) + (unsigned)(G::swz(r, phys) << 4);
+      } else {
+        const int r0 = (blk - G::A_BYTES / 1024) * G::ROWS_PER_KB;  // first LDS row, 0..255
+        const bool w3 = SWIGLU && r0 >= 128;
+        int n = t.n0 + (SWIGLU ? (r0 & 127) : r0);
+        int lim = a.Nout - 1 - n;  // rows past the last weight row repeat it
+        if (lim < 0) {
+          n = a.Nout - 1;
+          lim = 0;
+        }
+        if (a.B0x && t.g == a.n_groups - 1)  // the folded shared expert
+          base[j] = (const char*)(w3 ? a.B1x : a.B0x) + (int64_t)n * rowb;
+        else
+          base[j] = (const char*)(w3 ? a.B1 : a.B0) + ((int64_t)t.g * a.Nout + n) * rowb;
+        off[j] = (unsigned)((rib < lim ? rib : lim) * rowb) +
+                 (unsigned)(G::swz(r0 + rib, phys) << 4);
+      }
+    }
+  }
+
+  // Direct load j of the current step into `stage`.
+  __device__ __forceinline__ void load(int j, char* stage, int wv) const {
+    __builtin_amdgcn_global_load_lds((const void*)(base[j] + kt * (BK * 2) + off[j]),
+                                     (lds_void*)(stage + (NWAVE * j + wv) * 1024), 16, 0, 0);
+  }
+};
+
+// The gathered row indices of tile `t` into ri[b]: wave wv fetches 64 of them.
+__device__ __forceinline__ void fetch_rows(const GroupedGemmArgs& a, TileTab& tt, int b,
+                                           const Tile& t, int wv, int lane) {
+  int64_t gr = t.row0 + wv * 64 + lane;
+  if (gr > t.rend - 1) gr = t.rend - 1;
+  __builtin_amdgcn_global_load_lds((const void*)(a.row_index + gr),
+                                   (lds_void*)(&tt.ri[b][wv * 64]), 4, 0, 0);
+}
+
+struct Sched {
+  int n_groups, ntn, CN, lo, nslot, ntile;
+  __device__ __forceinline__ int tile_id(int i) const { return lo + i * nslot; }
+};
+
+// Advances the issuer past the step it has just loaded; on entering a new
+// tile, rebuilds the sources (from row indices fetched a tile earlier) and
+// fetches the row indices of the tile after it.  Past the last tile the last
+// step is loaded again, into stages that are never read.
+template <int BK, bool SWIGLU>
+__device__ __forceinline__ void advance(Issuer<BK, SWIGLU>& is, const GroupedGemmArgs& a,
+                                        TileTab& tt, const Sched& sc, int nk, int wv, int lane) {
+  if (++is.kt < nk) return;
+  if (is.it + 1 >= sc.ntile) {
+    is.kt = nk - 1;
+    return;
+  }
+  ++is.it;
+  is.kt = 0;
+  const Tile t = decode_tile(tt, sc.n_groups, sc.ntn, sc.CN, sc.tile_id(is.it));
+  is.build(a, tt, t, wv, lane);
+  if (a.row_index && is.it + 1 < sc.ntile)
+    fetch_rows(a, tt, (is.it + 1) & 1,
+               decode_tile(tt, sc.n_groups, sc.ntn, sc.CN, sc.tile_id(is.it + 1)), wv, lane);
+}
+
+// Stores the finished tile: SwiGLU (up) or plain (down), bf16, 16 bytes per
+// lane.  Lane l holds output row l&31 of each 32-row block and columns
+// 8*q + 4*(l>>5) + 0..3 (q = 0..3) of each 32-column tile; after the swap
+// with lane l^32, lane l holds columns 16*p + 8*(l>>5) + 0..7 (p = 0, 1).
+template <bool SWIGLU>
+__device__ __forceinline__ void store_tile(const GroupedGemmArgs& a, const Tile& t, int nbw,
+                                           int wm, int wn, int lane, f32x16_t (&acc)[MB][NT]) {
+  constexpr int NJ = SWIGLU ? NT / 2 : NT;
+  constexpr int WCOLS = SWIGLU ? 64 : 128;  // output columns per wave
+  bf16_t* __restrict__ C = (bf16_t*)a.C;
+  const int hi = lane >> 5;
+  const int64_t nrows = t.rend - t.row0;
+#pragma unroll
+  for (int i = 0; i < MB; ++i) {
+    if (i >= nbw) break;
+    const int m = (2 * i + wm) * 32 + (lane & 31);
+    const bool row_ok = m < nrows;
+    bf16_t* crow = C + (t.row0 + m) * a.Nout;
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) {
+      // keep the accumulators in the AGPRs until their tile is stored (else
+      // the compiler copies all of them to VGPRs at once, and spills)
+      asm volatile("" : "+a"(acc[i][j]));
+      if (SWIGLU) asm volatile("" : "+a"(acc[i][j + 2]));
+      unsigned p[4][2];
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          float v0, v1;
+          if (SWIGLU) {
+            const float g0 = acc[i][j][4 * q + 2 * h], u0 = acc[i][j + 2][4 * q + 2 * h];
+            const float g1 = acc[i][j][4 * q + 2 * h + 1], u1 = acc[i][j + 2][4 * q + 2 * h + 1];
+            v0 = g0 * __builtin_amdgcn_rcpf(1.f + __expf(-g0)) * u0;
+            v1 = g1 * __builtin_amdgcn_rcpf(1.f + __expf(-g1)) * u1;
+          } else {
+            v0 = acc[i][j][4 * q + 2 * h];
+            v1 = acc[i][j][4 * q + 2 * h + 1];
+          }
+          // v_cvt_pk_bf16_f32: round to nearest even
+          const bf16x2_t pk = {(__bf16)v0, (__bf16)v1};
+          p[q][h] = __builtin_bit_cast(unsigned, pk);
+        }
+#pragma unroll
+      for (int pp = 0; pp < 2; ++pp) {
+        // lanes 0-31 give their run 2pp+1 to lanes 32-63 and take those
+        // lanes' run 2pp
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          const auto r = __builtin_amdgcn_permlane32_swap(p[2 * pp][h], p[2 * pp + 1][h], false,
+                                                          false);
+          p[2 * pp][h] = r[0];
+          p[2 * pp + 1][h] = r[1];
+        }
+        const int col = t.n0 + wn * WCOLS + j * 32 + 16 * pp + 8 * hi;
+        if (row_ok && col < a.Nout) {
+          const u32x4_t v = {p[2 * pp][0], p[2 * pp][1], p[2 * pp + 1][0], p[2 * pp + 1][1]};
+          *(u32x4_t*)(crow + col) = v;
+        }
+      }
+      // one 32x32 tile at a time: keeps the accumulators in the AGPRs
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  }
+}
+
+// The steps of one tile for a wave with NB valid 32-row blocks.  Step g of
+// the sequence reads stage g % NS; during it the loads of step g+NS-1 go into
+// stage (g-1) % NS, which every wave finished reading before barrier B(g).
+// B(g+1) follows this thread's wait for its loads of step g+1 and for all its
+// LDS reads: after it step g+1 has landed for every thread.
+template <int BK, int NS, bool SWIGLU, int NB>
+__device__ __forceinline__ void run_tile(int& g, int nk, Issuer<BK, SWIGLU>& is,
+                                         const GroupedGemmArgs& a, TileTab& tt, const Sched& sc,
+                                         char (*st)[Geo<BK>::STAGE_BYTES], int wm, int wn, int wv,
+                                         int lane, Frags (&f)[2], f32x16_t (&acc)[MB][NT]) {
+  using G = Geo<BK>;
+  constexpr int KS = G::KS, LOADS = G::LOADS;
+  // row groups of four MFMAs before the barrier of a step, and the loads
+  // issued after each
+  constexpr int GROUPS = 4 * (KS - 1) + 2;
+  for (int kt = 0; kt < nk; ++kt, ++g) {
+    const char* cur = st[g % NS];
+    char* dst = st[(g + NS - 1) % NS];
+#pragma unroll
+    for (int s = 0; s < KS; ++s) {
+      const Frags& fc = f[s & 1];
+      Frags& fn = f[(s + 1) & 1];
+#pragma unroll
+      for (int i = 0; i < MB; ++i) {
+        const int grp = 4 * s + i;
+        if (s == KS - 1 && i == 2) {
+          // B(g+1), then the fragments of the next step's first k-step
+          wait_vm_lgkm<(NS - 2) * LOADS>();
+          __builtin_amdgcn_s_barrier();
+          read_frags<BK, SWIGLU>(st[(g + 1) % NS], 0, wm, wn, lane, fn);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+        mfma_row<NB>(i, fc, acc);
+        __builtin_amdgcn_sched_barrier(0);
+        if (grp < GROUPS) {
+          // spread the LOADS loads of step g+NS-1 over the groups before B(g+1)
+          const int upto = (LOADS * (grp + 1)) / GROUPS;
+#pragma unroll
+          for (int j = 0; j < LOADS; ++j)
+            if (j >= (LOADS * grp) / GROUPS && j < upto) is.load(j, dst, wv);
+          if (grp == GROUPS - 1) advance<BK, SWIGLU>(is, a, tt, sc, nk, wv, lane);
+        }
+        if (i == 0 && s < KS - 1) read_frags<BK, SWIGLU>(cur, s + 1, wm, wn, lane, fn);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+  }
+}
+
+template <int BK, int NS, bool SWIGLU, int NB>
+__device__ __forceinline__ void run_tile_dispatch(int nbw, int& g, int nk, Issuer<BK, SWIGLU>& is,
+                                                  const GroupedGemmArgs& a, TileTab& tt,
+                                                  const Sched& sc,
+                                                  char (*st)[Geo<BK>::STAGE_BYTES], int wm, int wn,
+                                                  int wv, int lane, Frags (&f)[2],
+                                                  f32x16_t (&acc)[MB][NT]) {
+  if (nbw == NB || NB == 0)
+    run_tile<BK, NS, SWIGLU, NB>(g, nk, is, a, tt, sc, st, wm, wn, wv, lane, f, acc);
+  else if constexpr (NB > 0)
+    run_tile_dispatch<BK, NS, SWIGLU, NB - 1>(nbw, g, nk, is, a, tt, sc, st, wm, wn, wv, lane, f,
+                                              acc);
+}
+
+template <int BK, int NS, bool SWIGLU>
+__global__ __launch_bounds__(NTHR, 1) void gemm_bf16_persist_kernel(GroupedGemmArgs args) {
+  using G = Geo<BK>;
+  // one LDS object: the stages, then the tile table
+  __shared__ __attribute__((aligned(1024))) char smem[NS * G::STAGE_BYTES + sizeof(TileTab)];
+  char(*st)[G::STAGE_BYTES] = (char(*)[G::STAGE_BYTES])smem;
+  TileTab& tt = *(TileTab*)(smem + NS * G::STAGE_BYTES);
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wv >> 1, wn = wv & 1;
+  constexpr int CN = SWIGLU ? BN / 2 : BN;
+
+  // per-group M-tile prefix and row offsets, in LDS for the whole kernel
+  const int total_m =
+      group_tile_prefix<NTHR>(args.offsets, args.n_groups, BM, tt.ts, tt.off, tt.scan);
+  __syncthreads();
+
+  Sched sc;
+  sc.n_groups = args.n_groups;
+  sc.CN = CN;
+  sc.ntn = (args.Nout + CN - 1) / CN;
+  const int total = total_m * sc.ntn;
+  sc.nslot = gridDim.x / kNumXcd;
+  const int xcd = blockIdx.x % kNumXcd, slot = blockIdx.x / kNumXcd;
+  const int per = (total + kNumXcd - 1) / kNumXcd;
+  const int lo = xcd * per, hi = min(lo + per, total);
+  sc.lo = lo + slot;
+  if (sc.lo >= hi) return;
+  sc.ntile = (hi - sc.lo + sc.nslot - 1) / sc.nslot;
+  const int nk = args.K / BK;
+
+  // tile 0's row indices, then the sources of its first steps
+  Tile t = decode_tile(tt, sc.n_groups, sc.ntn, CN, sc.tile_id(0));
+  if (args.row_index) {
+    fetch_rows(args, tt, 0, t, wv, lane);
+    wait_vm_lgkm<0>();
+    __syncthreads();
+  }
+  Issuer<BK, SWIGLU> is;
+  is.it = 0;
+  is.kt = 0;
+  is.build(args, tt, t, wv, lane);
+  if (args.row_index && sc.ntile > 1)
+    fetch_rows(args, tt, 1, decode_tile(tt, sc.n_groups, sc.ntn, CN, sc.tile_id(1)), wv, lane);
+  // steps 0 .. NS-2 into stages 0 .. NS-2
+#pragma unroll
+  for (int s = 0; s < NS - 1; ++s) {
+#pragma unroll
+    for (int j = 0; j < G::LOADS; ++j) is.load(j, st[s], wv);
+    advance<BK, SWIGLU>(is, args, tt, sc, nk, wv, lane);
+  }
+  // The row indices of the tile after the next are fetched when the issuer
+  // enters a tile and read when it enters the next one, at least NS-1 steps
+  // (one barrier) later only if a tile has NS-1 steps or more.
+  wait_vm_lgkm<(NS - 2) * G::LOADS>();
+  __builtin_amdgcn_s_barrier();  // B(0)
+
+  Frags f[2];
+  read_frags<BK, SWIGLU>(st[0], 0, wm, wn, lane, f[0]);
+  f32x16_t acc[MB][NT];
+  int g = 0;
+  for (int i = 0; i < sc.ntile; ++i) {
+    if (i > 0) t = decode_tile(tt, sc.n_groups, sc.ntn, CN, sc.tile_id(i));
+    const int64_t nrows64 = t.rend - t.row0;
+    const int nrows = nrows64 < BM ? (int)nrows64 : BM;
+    // row block i of wave row wm is block 2i+wm of the tile
+    int nbw = (((nrows + 31) >> 5) - wm + 1) >> 1;
+    nbw = nbw < 0 ? 0 : (nbw > MB ? MB : nbw);
+#pragma unroll
+    for (int r = 0; r < MB; ++r)
+#pragma unroll
+      for (int c = 0; c < NT; ++c)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) acc[r][c][e] = 0.f;
+    run_tile_dispatch<BK, NS, SWIGLU, MB>(nbw, g, nk, is, args, tt, sc, st, wm, wn, wv, lane, f,
+                                          acc);
+    store_tile<SWIGLU>(args, t, nbw, wm, wn, lane, acc);
+  }
+  // no load may still be writing LDS when the workgroup ends
+  wait_vm_lgkm<0>();
+}
+
+constexpr int LIB_BK = 32, LIB_NS = 4;
+
+}  // namespace gp
+
+int persist_grid() {
+  static int grid = [] {
+    int dev = 0, cus = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        cus < kNumXcd)
+      cus = 256;
+    return (cus / kNumXcd) * kNumXcd;
+  }();
+  return grid;
+}
+
+hipError_t launch_gemm_bf16_persist(const GroupedGemmArgs& a, bool swiglu, hipStream_t s) {
+  if (a.max_rows <= 0 || a.n_groups <= 0) return hipSuccess;
+  const int grid = persist_grid();
+  if (swiglu)
+    gp::gemm_bf16_persist_kernel<gp::LIB_BK, gp::LIB_NS, true><<<grid, gp::NTHR, 0, s>>>(a);
+  else
+    gp::gemm_bf16_persist_kernel<gp::LIB_BK, gp::LIB_NS, false><<<grid, gp::NTHR, 0, s>>>(a);
+  return hipGetLastError();
+}
+
+}  // namespace moe

@@ -200,15 +200,16 @@ __global__ __launch_bounds__(NWAVE * 64, 1) void gemm_bf16_v2_kernel(GroupedGemm
       const int r = (blk - G::A_BYTES / 1024) * G::ROWS_PER_KB + rib;  // 0..255
       const bf16_t* Bm;
       int n;
+      const bool xg = args.B0x && tc.group == args.n_groups - 1;  // folded shared expert
       if (SWIGLU) {
-        Bm = (const bf16_t*)(r < 128 ? args.B0 : args.B1);
+        Bm = (const bf16_t*)(r < 128 ? (xg ? args.B0x : args.B0) : (xg ? args.B1x : args.B1));
         n = tc.n0 + (r & 127);
       } else {
-        Bm = (const bf16_t*)args.B0;
+        Bm = (const bf16_t*)(xg ? args.B0x : args.B0);
         n = tc.n0 + r;
       }
       if (n > Nout - 1) n = Nout - 1;
-      src[j] = Bm + ((int64_t)tc.group * Nout + n) * K + G::swz(r, phys) * 8;
+      src[j] = Bm + ((int64_t)(xg ? 0 : tc.group) * Nout + n) * K + G::swz(r, phys) * 8;
     }
   }
 

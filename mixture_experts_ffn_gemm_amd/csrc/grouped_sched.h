@@ -18,7 +18,7 @@
 
 namespace moe {
 
-constexpr int kMaxGroups = 256;
+constexpr int kMaxGroups = 512;  // routed experts (<= 256) + a folded shared expert
 constexpr int kNumXcd = 8;
 
 struct TileCoord {
@@ -27,6 +27,44 @@ struct TileCoord {
   int64_t rend;  // end of the group's rows
   int n0;        // first output column
 };
+
+// ts[g] = number of BM-row tiles of groups 0..g-1 (ts[0] = 0), for up to
+// kMaxGroups groups: thread t takes groups t*PER .. t*PER+PER-1.  If `off` is
+// non-null it receives the group row offsets.  Returns the total; must be
+// called by all NT threads of the block; ts/off are complete after a barrier.
+template <int NT>
+__device__ __forceinline__ int group_tile_prefix(const int32_t* __restrict__ offsets,
+                                                 int n_groups, int BM, int* ts, int* off,
+                                                 int* s_scratch /* NT/64 */) {
+  constexpr int PER = (kMaxGroups + NT - 1) / NT;
+  const int tid = threadIdx.x;
+  int mt[PER];
+  int sum = 0;
+#pragma unroll
+  for (int q = 0; q < PER; ++q) {
+    const int g = tid * PER + q;
+    mt[q] = 0;
+    if (g < n_groups) {
+      const int o0 = offsets[g], o1 = offsets[g + 1];
+      mt[q] = (o1 - o0 + BM - 1) / BM;
+      if (off) {
+        off[g] = o0;
+        if (g == n_groups - 1) off[g + 1] = o1;
+      }
+    }
+    sum += mt[q];
+  }
+  int total;
+  int run = block_incl_scan<NT>(sum, s_scratch, &total) - sum;
+#pragma unroll
+  for (int q = 0; q < PER; ++q) {
+    const int g = tid * PER + q;
+    run += mt[q];
+    if (g < n_groups) ts[g + 1] = run;
+  }
+  if (tid == 0) ts[0] = 0;
+  return total;
+}
 
 // Must be called by all NT threads of the block.  Returns false when the
 // block has no tile (uniformly for the whole block).
@@ -37,15 +75,7 @@ __device__ __forceinline__ bool grouped_tile_lookup(const int32_t* __restrict__ 
                                                     int* s_scratch /* NT/64 */, int* s_info,
                                                     TileCoord* tc) {
   const int tid = threadIdx.x;
-  int tiles = 0;
-  if (tid < n_groups) {
-    const int cnt = offsets[tid + 1] - offsets[tid];
-    tiles = (cnt + BM - 1) / BM;
-  }
-  int total_m;
-  const int incl = block_incl_scan<NT>(tiles, s_scratch, &total_m);
-  if (tid < n_groups) s_ts[tid + 1] = incl;
-  if (tid == 0) s_ts[0] = 0;
+  const int total_m = group_tile_prefix<NT>(offsets, n_groups, BM, s_ts, nullptr, s_scratch);
   const int n_tiles_n = (Nout + BN - 1) / BN;
   const int total = total_m * n_tiles_n;
   const int per = (total + kNumXcd - 1) / kNumXcd;
@@ -55,9 +85,9 @@ __device__ __forceinline__ bool grouped_tile_lookup(const int32_t* __restrict__ 
   const int L = xcd * per + j;
   if (L >= total) return false;
   __syncthreads();
-  if (tid < n_groups) {
-    const int lo = s_ts[tid] * n_tiles_n, hi = s_ts[tid + 1] * n_tiles_n;
-    if (L >= lo && L < hi) s_info[0] = tid;
+  for (int g = tid; g < n_groups; g += NT) {
+    const int lo = s_ts[g] * n_tiles_n, hi = s_ts[g + 1] * n_tiles_n;
+    if (L >= lo && L < hi) s_info[0] = g;
   }
   __syncthreads();
   const int g = s_info[0];

@@ -58,6 +58,9 @@ hipError_t launch_permute(const int32_t* idx, int64_t T, int k, int N, int32_t* 
 hipError_t launch_fill_i32(int32_t* p, int64_t n, int32_t value, hipStream_t stream);
 // p[0] = 0, p[1] = n: the row range of a single group covering n rows
 hipError_t launch_set_range(int32_t* p, int32_t n, hipStream_t stream);
+// row_token_tail[t] = t for t < T, and offsets_last[0] = end
+hipError_t launch_append_shared_rows(int32_t* row_token_tail, int32_t T, int32_t* offsets_last,
+                                     int32_t end, hipStream_t stream);
 hipError_t launch_gather_rows(const void* x, const int32_t* row_token, void* x_perm,
                               int64_t rows, int64_t row_bytes, hipStream_t stream);
 
@@ -71,17 +74,19 @@ struct GroupedGemmArgs {
   int64_t max_rows;
   const void* B0;           // [G, Nout, K]  (W1 or W2)
   const void* B1;           // [G, Nout, K]  (W3) for the SwiGLU epilogue, else null
+  const void* B0x;          // bf16 only: if non-null, the weights [Nout, K] of the last
+  const void* B1x;          //   group (the shared expert folded in as one more group)
   const float* S0;          // fp8 block scales [G, Nout/128, K/128] or null
   const float* S1;
   void* C;                  // [rows, Nout]
   int Nout;
   int K;
 };
-// bf16 MFMA (act bf16, w bf16)
-hipError_t launch_gemm_bf16_swiglu(const GroupedGemmArgs& a, hipStream_t s);
-hipError_t launch_gemm_bf16_store(const GroupedGemmArgs& a, hipStream_t s);
 // second generation: 256x256 tiles, 8 wavefronts, direct-to-LDS 4-stage pipeline
 hipError_t launch_gemm_bf16_v2(const GroupedGemmArgs& a, bool swiglu, hipStream_t s);
+// persistent: one workgroup per CU, one pipeline across all of its tiles (K >= 128)
+hipError_t launch_gemm_bf16_persist(const GroupedGemmArgs& a, bool swiglu, hipStream_t s);
+int persist_grid();
 // fp32 SIMT (act f32, w f32)
 hipError_t launch_gemm_f32_swiglu(const GroupedGemmArgs& a, hipStream_t s);
 hipError_t launch_gemm_f32_store(const GroupedGemmArgs& a, hipStream_t s);

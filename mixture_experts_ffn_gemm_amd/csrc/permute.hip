@@ -134,6 +134,23 @@ hipError_t launch_set_range(int32_t* p, int32_t n, hipStream_t stream) {
   return hipGetLastError();
 }
 
+// The shared expert as one more group after the routed slots: its rows are
+// every token in order, and the group ends at slots + T.
+__global__ void append_shared_rows_kernel(int32_t* __restrict__ row_token_tail, int32_t T,
+                                          int32_t* __restrict__ offsets_last, int32_t end) {
+  const int32_t t = (int32_t)blockIdx.x * 256 + threadIdx.x;
+  if (t < T) row_token_tail[t] = t;
+  if (t == 0) offsets_last[0] = end;
+}
+
+hipError_t launch_append_shared_rows(int32_t* row_token_tail, int32_t T, int32_t* offsets_last,
+                                     int32_t end, hipStream_t stream) {
+  if (T <= 0) return hipSuccess;
+  append_shared_rows_kernel<<<(unsigned)cdiv(T, 256), 256, 0, stream>>>(row_token_tail, T,
+                                                                        offsets_last, end);
+  return hipGetLastError();
+}
+
 // x_perm[r] = x[row_token[r]]: one 256-thread block per row, 16-byte copies.
 typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
 __global__ __launch_bounds__(256) void gather_rows_kernel(const u32x4_t* __restrict__ x,

@@ -30,12 +30,16 @@ def rel_err(got: np.ndarray, ref: np.ndarray) -> float:
     return float(np.max(np.abs(got.astype(np.float64) - ref))) / max(rms, 1e-30)
 
 
+def round_bf16(v: np.ndarray) -> np.ndarray:
+    """Round to the nearest bfloat16 (ties to even), returned as float64."""
+    import torch
+    return torch.from_numpy(np.asarray(v, dtype=np.float32)).to(torch.bfloat16).double().numpy()
+
+
 def bf16_floor(ref: np.ndarray) -> float:
     """max |bf16(ref) - ref| / RMS(ref): the error a bf16 output has even when
     every value is the correctly rounded oracle value."""
-    import torch
-    r16 = torch.from_numpy(ref.astype(np.float32)).to(torch.bfloat16).double().numpy()
-    return rel_err(r16, ref)
+    return rel_err(round_bf16(ref), ref)
 
 
 def bf16_half_ulp(v: np.ndarray) -> np.ndarray:

@@ -12,7 +12,7 @@ import datagen
 import oracle
 from datagen.device import upload, to_torch
 from parity_util import (TIE, bf16_floor, bf16_half_ulp, check_routing, oracle_route, rel_err,
-                         say, tol_for)
+                         round_bf16, say, tol_for)
 
 pytestmark = [pytest.mark.gpu, pytest.mark.filterwarnings("ignore::RuntimeWarning")]
 
@@ -121,12 +121,20 @@ def _rows_and_offsets(counts):
     return off, int(off[-1])
 
 
-@pytest.mark.parametrize("wdt", ["f32", "bf16", "fp8"])
+@pytest.mark.parametrize("wdt", ["f32", "bf16", "fp8", "bf16_small_k", "bf16_many_tiles"])
 def test_expert_ffn_ragged_groups(lib, wdt):
-    """Groups of 0, 1, tile-1, tile, tile+1 and several tiles of rows."""
-    d, I = (256, 512) if wdt == "f32" else (512, 384)
+    """Groups of 0, 1, tile-1, tile, tile+1 and several tiles of rows.
+
+    bf16_small_k: K = 128 for both projections, the smallest K the bf16 path
+    takes (four 32-deep steps per tile, as many as the pipeline has stages).
+    bf16_many_tiles: more tiles than workgroups, so every persistent workgroup
+    runs its pipeline across several tiles of different experts and fills."""
+    d, I = {"f32": (256, 512), "bf16_small_k": (128, 128)}.get(wdt, (512, 384))
     counts = [0, 1, 127, 128, 129, 300, 0, 5, 64, 65]
-    name = {"f32": "gshard_fp32", "bf16": "deepseekmoe_2b", "fp8": "v3_decode"}[wdt]
+    if wdt == "bf16_many_tiles":
+        counts = [int(c) for c in np.random.default_rng(11).integers(0, 700, 72)]
+        counts[:6] = [0, 1, 255, 256, 257, 699]
+    name = {"f32": "gshard_fp32", "fp8": "v3_decode"}.get(wdt, "deepseekmoe_2b")
     cfg = datagen.get_config(name, d=d, inter=I, n_routed=len(counts), k=1, n_groups=1,
                              topk_groups=1, T=sum(counts), n_shared=0)
     say(f"[expert_ffn] {wdt} d={d} I={I} counts={counts}")
@@ -146,17 +154,38 @@ def test_expert_ffn_ragged_groups(lib, wdt):
     got = y.float().cpu().numpy()
     x64 = oracle.widen(x, cfg.act_dtype)[row_index]
     ref = np.zeros((rows, d))
+    ideal = np.zeros((rows, d))
     for e, n in enumerate(counts):
         if n == 0:
             continue
         w = oracle.expert_weights64(cfg, {k: (v[e] if v is not None else None) for k, v in ex.items()})
-        ref[off[e]:off[e + 1]] = oracle.swiglu(x64[off[e]:off[e + 1]], *w)
+        xs = x64[off[e]:off[e + 1]]
+        ref[off[e]:off[e + 1]] = oracle.swiglu(xs, *w)
+        if cfg.act_dtype == "bf16":
+            # the same contraction with h stored as bf16, as the kernels store it
+            g, u = xs @ w[0].T, xs @ w[1].T
+            ideal[off[e]:off[e + 1]] = round_bf16(g * oracle.sigmoid(g) * u) @ w[2].T
     err = rel_err(got, ref)
-    floor = bf16_floor(ref) if cfg.act_dtype == "bf16" else 0.0
-    say(f"   rel err {err:.3e} (bf16 output rounding alone: {floor:.3e})")
-    assert err < tol_for(cfg)
-    # beyond the output rounding, only the bf16 rounding of h and fp32 sums
-    assert err <= floor + (1e-2 if cfg.act_dtype == "bf16" else 2e-5)
+    if cfg.act_dtype != "bf16":
+        say(f"   rel err {err:.3e}")
+        assert err < tol_for(cfg)
+        assert err <= 2e-5
+        return
+    # The error of the correctly rounded bf16 pipeline (h and the output
+    # rounded to bf16, everything else exact) bounds what any kernel storing
+    # bf16 can reach; the kernel may add fp32 summation noise and flip a few
+    # rounding decisions on top of it.
+    ideal_err = rel_err(round_bf16(ideal), ref)
+    floor = bf16_floor(ref)
+    say(f"   rel err {err:.3e} (correctly rounded bf16 pipeline: {ideal_err:.3e}; "
+        f"output rounding alone: {floor:.3e})")
+    assert err <= ideal_err + 0.25 * floor
+    if ideal_err < tol_for(cfg):
+        assert err < tol_for(cfg)
+    else:
+        # at this shape no bf16-output pipeline meets the bf16 bar (a few
+        # outputs are many times the RMS): the bound above is the check
+        say(f"   bf16 bar {tol_for(cfg)} unreachable here: rounded pipeline alone is {ideal_err:.3e}")
 
 
 # ---------------------------------------------------------------- combine
@@ -197,20 +226,20 @@ def test_combine(lib, act, out):
 # ---------------------------------------------------------------- forward
 
 
-def _run_forward(lib, cfg, dev_inputs, **kw):
+def _run_forward(lib, cfg, dev_inputs, side=True, **kw):
     c = lib.config_from(cfg)
-    side = torch.cuda.Stream()
     out, idx, gate, counts = lib.forward(c, dev_inputs["x"], dev_inputs["w_r"], dev_inputs["b"],
                                          dev_inputs["experts"], dev_inputs["shared"],
-                                         want_routing=True, side_stream=side, **kw)
+                                         want_routing=True,
+                                         side_stream=torch.cuda.Stream() if side else None, **kw)
     torch.cuda.synchronize()
     return out, idx.cpu().numpy(), gate.cpu().numpy(), counts.cpu().numpy()
 
 
-def _forward_parity(lib, cfg, tokens=None):
+def _forward_parity(lib, cfg, tokens=None, side=True):
     inp = datagen.MoEInputs(cfg)
     dev = upload(inp)
-    out, idx, gate, counts = _run_forward(lib, cfg, dev)
+    out, idx, gate, counts = _run_forward(lib, cfg, dev, side=side)
     x = inp.x()
     r = oracle_route(cfg, inp, x)
     near, order = check_routing(cfg, r, idx, gate)
@@ -259,6 +288,21 @@ def test_forward_deterministic_and_bf16_out(lib):
     c16 = _run_forward(lib, cfg16, dev)[0]
     assert c16.dtype == torch.bfloat16
     assert torch.equal(c16, a.to(torch.bfloat16))
+
+
+@pytest.mark.parametrize("name", ["deepseekmoe_2b", "v2_shaped", "v3_prefill"])
+def test_forward_one_stream(lib, name):
+    """Without a second stream the one shared expert of bf16 layers runs as one
+    more group of the routed grouped GEMMs (V3: 256 routed + 1 shared groups);
+    the result is bitwise that of the two-stream forward."""
+    cfg = small_cfg(name)
+    say(f"[forward-one-stream] {name} N={cfg.n_routed} S={cfg.n_shared}")
+    inp = datagen.MoEInputs(cfg)
+    dev = upload(inp)
+    a = _run_forward(lib, cfg, dev, side=True)[0]
+    b = _run_forward(lib, cfg, dev, side=False)[0]
+    assert torch.equal(a, b)
+    _forward_parity(lib, cfg, side=False)
 
 
 def test_forward_empty_batch(lib):
