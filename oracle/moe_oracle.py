@@ -181,18 +181,65 @@ def gate_values(gate: str, route_scale: float, value: np.ndarray, idx: np.ndarra
     return route_scale * sel / sel.sum(axis=1, keepdims=True)
 
 
-def route(cfg, x64: np.ndarray, wr64: np.ndarray, b=None) -> dict:
+def exclude_experts(key: np.ndarray, allow=None, mask_top: int = 0):
+    """Keys with experts taken out of the selection.
+
+    aiany.app explainer, Step 9, probe 1: for each token the routed experts the
+    router wanted most are masked and the token routes among the rest.  Here
+    ``allow`` (bool [N], optional) first removes a fixed expert set, then each
+    token's ``mask_top`` highest remaining keys (key descending, index
+    ascending, as in the top-k) are removed.  Removed keys become -inf; the
+    scores themselves (softmax probabilities, sigmoid values) are unchanged.
+    Returns (keys, margin) with margin = the mask_top-th minus the next
+    remaining key (inf when nothing is masked per token)."""
+    masked = np.array(key, dtype=np.float64, copy=True)
+    if allow is not None:
+        masked[:, ~np.asarray(allow, bool)] = -np.inf
+    margin = np.full(masked.shape[0], np.inf)
+    if mask_top > 0:
+        order = _ranked(masked)
+        last = np.take_along_axis(masked, order[:, mask_top - 1:mask_top], 1)[:, 0]
+        nxt = np.take_along_axis(masked, order[:, mask_top:mask_top + 1], 1)[:, 0]
+        margin = last - nxt
+        np.put_along_axis(masked, order[:, :mask_top], -np.inf, axis=1)
+    return masked, margin
+
+
+def route(cfg, x64: np.ndarray, wr64: np.ndarray, b=None, allow=None, mask_top: int = 0) -> dict:
     """Router of the layer for every token of x64.  cfg needs k, n_groups,
-    topk_groups, group_topn, gate, route_scale, n_routed."""
+    topk_groups, group_topn, gate, route_scale, n_routed.  ``allow`` and
+    ``mask_top`` take experts out of the selection (``exclude_experts``)."""
     z = router_logits(x64, wr64)
     value, key = router_scores(cfg.gate, z, b)
-    allowed, gscore, gmargin = group_limit(key, cfg.n_groups, cfg.topk_groups, cfg.group_topn)
-    idx, kmargin = topk_select(key, allowed, cfg.k)
+    key_sel, mmargin = exclude_experts(key, allow, mask_top)
+    allowed, gscore, gmargin = group_limit(key_sel, cfg.n_groups, cfg.topk_groups,
+                                           cfg.group_topn)
+    idx, kmargin = topk_select(key_sel, allowed, cfg.k)
     gates = gate_values(cfg.gate, cfg.route_scale, value, idx)
     counts = np.bincount(idx.ravel(), minlength=cfg.n_routed)
     return dict(z=z, value=value, key=key, allowed=allowed, group_scores=gscore,
-                idx=idx, gates=gates, counts=counts, margin=np.minimum(kmargin, gmargin),
-                kmargin=kmargin, gmargin=gmargin)
+                idx=idx, gates=gates, counts=counts,
+                margin=np.minimum(np.minimum(kmargin, gmargin), mmargin),
+                kmargin=kmargin, gmargin=gmargin, mmargin=mmargin)
+
+
+def bias_update(b, counts, slots: int, gamma: float) -> np.ndarray:
+    """Auxiliary-loss-free balancing step.
+
+    grasp.study lesson, 3.2 "Auxiliary-Loss-Free Load Balancing": after a batch,
+    each expert's selection bias moves by a fixed step, up when the expert was
+    underloaded and down when it was overloaded (shivam2003.com "5.6", the
+    V3 column of the configuration table: balancing by that bias instead of
+    auxiliary losses).  Reading: the load of expert i is its count of the
+    ``slots`` = T*k selections, the reference is the mean slots/N, the step is
+    gamma * sign(mean - load_i) (no change at exactly the mean); the sign is
+    decided on integers (N*load_i against slots); b is the fp32 router bias, so
+    the updated value is rounded to fp32 once."""
+    counts = np.asarray(counts, np.int64)
+    n = counts.size
+    sgn = np.sign(np.int64(slots) - counts * n).astype(np.float64)
+    return (np.asarray(b, np.float32).astype(np.float64) +
+            np.float64(np.float32(gamma)) * sgn).astype(np.float32)
 
 
 def stable_permutation(idx: np.ndarray, n_routed: int) -> dict:

@@ -415,3 +415,121 @@ def test_datagen_streams_are_independent_per_expert():
     assert np.array_equal(stacked["w1"][1], a)
     x = inp.x()
     assert np.array_equal(inp.x_rows(100, 290), x[100:290])
+
+
+# ---------------------------------------------------------------- probes 1-2 and balancing
+
+
+def test_mask_top_brute_force():
+    """aiany.app Step 9, probe 1: mask each token's favourite experts and route
+    among the rest.  Brute force over all k-subsets of the experts outside the
+    token's m best keys; the margin is the m-th minus the (m+1)-th key."""
+    rng = np.random.default_rng(21)
+    for trial in range(150):
+        n = int(rng.integers(3, 12))
+        m = int(rng.integers(1, n - 1))
+        k = int(rng.integers(1, n - m + 1))
+        key = rng.standard_normal(n)
+        masked, margin = oracle.exclude_experts(key[None, :], None, m)
+        idx, _ = oracle.topk_select(masked, np.ones((1, n), bool), k)
+        favourites = set(np.argsort(-key)[:m].tolist())
+        rest = [e for e in range(n) if e not in favourites]
+        best = max(itertools.combinations(rest, k), key=lambda s: key[list(s)].sum())
+        assert set(idx[0].tolist()) == set(best)
+        srt = np.sort(key)[::-1]
+        assert np.isclose(margin[0], srt[m - 1] - srt[m])
+
+
+def test_mask_top_grouped_brute_force():
+    """Probe 1 under group-limited routing: group scores and the top-k use the
+    keys left after masking (brute force on the masked keys)."""
+    rng = np.random.default_rng(23)
+    for trial in range(100):
+        n_groups, gs = 4, 4
+        n = n_groups * gs
+        m = int(rng.integers(1, 3))
+        topk_groups = int(rng.integers(1, n_groups + 1))
+        k = int(rng.integers(1, topk_groups * (gs - m) + 1))
+        key = rng.standard_normal(n)
+        masked, _ = oracle.exclude_experts(key[None, :], None, m)
+        allowed, _, _ = oracle.group_limit(masked, n_groups, topk_groups, 2)
+        idx, _ = oracle.topk_select(masked, allowed, k)
+        fav = np.argsort(-key)[:m]
+        kk = key.copy()
+        kk[fav] = -1e9  # masked experts can never win a group score or a pick
+        assert set(idx[0].tolist()) == _brute_grouped(kk, n_groups, topk_groups, 2, k)
+        assert not set(fav.tolist()) & set(idx[0].tolist())
+
+
+def test_allow_set_and_no_mask_identity():
+    rng = np.random.default_rng(22)
+    cfg = Cfg(n_routed=16, k=3)
+    x = rng.standard_normal((64, 8))
+    wr = rng.standard_normal((16, 8))
+    base = oracle.route(cfg, x, wr)
+    same = oracle.route(cfg, x, wr, allow=np.ones(16, bool), mask_top=0)
+    assert np.array_equal(base["idx"], same["idx"]) and np.array_equal(base["gates"], same["gates"])
+    allow = np.ones(16, bool)
+    allow[[0, 5, 9]] = False
+    r = oracle.route(cfg, x, wr, allow=allow)
+    assert not np.isin(r["idx"], [0, 5, 9]).any()
+    # softmax gates stay the unmasked router's probabilities of the experts kept
+    assert np.allclose(r["gates"], np.take_along_axis(base["value"], r["idx"], 1))
+
+
+@pytest.mark.parametrize("gate", ["softmax", "sigmoid"])
+def test_fewer_picks_is_a_prefix(gate):
+    """aiany.app Step 9, probe 2: 4 picks instead of 7 select the first 4 of the
+    7 (same order); softmax gates are the same values, sigmoid gates are
+    renormalised over the 4 (scale 2.5 over the kept s)."""
+    rng = np.random.default_rng(24)
+    x = rng.standard_normal((128, 16))
+    wr = rng.standard_normal((32, 16))
+    kw = dict(n_routed=32, gate=gate, route_scale=1.0 if gate == "softmax" else 2.5)
+    if gate == "sigmoid":
+        kw.update(n_groups=4, topk_groups=2)
+    r7 = oracle.route(Cfg(k=7, **kw), x, wr)
+    r4 = oracle.route(Cfg(k=4, **kw), x, wr)
+    assert np.array_equal(r4["idx"], r7["idx"][:, :4])
+    if gate == "softmax":
+        assert np.array_equal(r4["gates"], r7["gates"][:, :4])
+    else:
+        s4 = np.take_along_axis(r7["value"], r7["idx"][:, :4], 1)
+        assert np.allclose(r4["gates"].sum(axis=1), 2.5)
+        assert np.allclose(r4["gates"], 2.5 * s4 / s4.sum(axis=1, keepdims=True))
+
+
+def test_bias_update_direction_and_step():
+    """grasp.study lesson 3.2: underloaded experts' biases go up, overloaded ones
+    go down, by the fixed step; loads at the mean leave the bias alone.  The
+    labels are worked by hand: 12 selections over 6 experts, mean 2."""
+    counts = np.array([3, 1, 2, 2, 0, 4])
+    label = np.array([-1, +1, 0, 0, +1, -1])  # over, under, at, at, under, over
+    b = np.array([0.1, -0.2, 0.05, 0.0, 1.5, -3.0], np.float32)
+    nb = oracle.bias_update(b, counts, 12, 0.01)
+    assert nb.dtype == np.float32
+    d = nb.astype(np.float64) - b.astype(np.float64)
+    assert np.array_equal(np.sign(d), label)
+    ulp = np.spacing(np.abs(b)).astype(np.float64)
+    assert np.all(np.abs(d - 0.01 * label) <= ulp + np.spacing(np.float32(0.01)))
+    assert np.array_equal(oracle.bias_update(b, [2] * 6, 12, 0.01), b)
+
+
+def test_bias_update_balances_routing():
+    """The step steers routing towards balance: starting from a bias that favours
+    a few experts, repeated route -> count -> update brings the busiest expert
+    from over 3x the mean load to within 25% of it."""
+    rng = np.random.default_rng(0)
+    N, k, T, d = 16, 2, 512, 32
+    x = rng.standard_normal((T, d))
+    wr = rng.standard_normal((N, d)) / np.sqrt(d)
+    cfg = Cfg(n_routed=N, k=k, gate="sigmoid", route_scale=1.0)
+    b = np.linspace(0.3, -0.3, N).astype(np.float32)
+    mean = T * k / N
+    first = None
+    for _ in range(150):
+        c = oracle.route(cfg, x, wr, b)["counts"]
+        first = c.max() / mean if first is None else first
+        b = oracle.bias_update(b, c, T * k, 0.005)
+    last = oracle.route(cfg, x, wr, b)["counts"].max() / mean
+    assert first > 3.0 and last < 1.25
