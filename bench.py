@@ -97,7 +97,36 @@ def traffic_from_profile(kernel_key: str, sources, algorithmic_per_launch):
     return ent.get("hbm_bytes_per_launch")
 
 
-def run_workload(name, steps, warmup, events: HipEvents):
+def time_next_rows(moe, c, dev, counts, events: HipEvents, stream, reps=20):
+    """Event-timed averages on the workload's own inputs: the router alone, the
+    router with each token's favourite expert masked (probe 1), and the
+    aux-loss-free bias step on the forward's counts."""
+    import torch
+    b = dev["b"] if dev["b"] is not None else torch.zeros(c.n_routed, device="cuda")
+    b = b.clone()
+    calls = {
+        "router_ms": lambda: moe.router(c, dev["x"], dev["w_r"], b),
+        "router_mask_top1_ms": lambda: moe.router_masked(c, dev["x"], dev["w_r"], b, mask_top=1),
+        "bias_update_ms": lambda: moe.bias_update(c, b, counts, 1e-3),
+    }
+    out = {}
+    for name, fn in calls.items():
+        fn()
+        torch.cuda.synchronize()
+        e0, e1 = events.create(2)
+        rec = events.hip.hipEventRecord
+        rec.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+        rec(e0, stream.cuda_stream)
+        for _ in range(reps):
+            fn()
+        rec(e1, stream.cuda_stream)
+        torch.cuda.synchronize()
+        out[name] = round(events.elapsed_ms(e0, e1) / reps, 4)
+        events.destroy([e0, e1])
+    return out
+
+
+def run_workload(name, steps, warmup, events: HipEvents, extra=False):
     import torch
     import datagen
     from datagen.device import upload
@@ -153,6 +182,8 @@ def run_workload(name, steps, warmup, events: HipEvents):
     counts_np = counts.cpu().numpy()
     res = dict(cfg=cfg, elapsed=elapsed, ms_per_step=elapsed / steps * 1e3, stage_ms=avg,
                counts=counts_np, inputs=inp)
+    if extra:
+        res["next_rows"] = time_next_rows(moe, c, dev, counts, events, main)
     del dev, out
     torch.cuda.empty_cache()
     return res
@@ -196,7 +227,7 @@ def decode_summary(r):
     }
 
 
-def cpu_baseline(inp, sample_tokens=8):
+def cpu_baseline(inp, sample_tokens=48):
     """The fp64 oracle (unchanged) on the first `sample_tokens` tokens of the
     workload: routing of those tokens plus their routed and shared experts."""
     import numpy as np
@@ -348,7 +379,7 @@ def main():
     events = HipEvents()
     if args.copy_calibration:
         copy_calibration()
-    r = run_workload(args.workload, args.steps, args.warmup, events)
+    r = run_workload(args.workload, args.steps, args.warmup, events, extra=True)
     cfg = r["cfg"]
     value = cfg.T * args.steps / r["elapsed"]
     flops = cfg.flops_per_token() * cfg.T
@@ -363,6 +394,7 @@ def main():
         "layer_mfma_frac": round(flops / (r["ms_per_step"] * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
         "stage_ms": {k: round(v, 4) for k, v in r["stage_ms"].items()},
         "roofline": prefill_roofline(r),
+        "next_rows": r.get("next_rows"),
     }
     inp = r.pop("inputs")
     if not args.no_decode:

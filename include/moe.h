@@ -114,6 +114,39 @@ int moe_router(const moe_config* cfg, const void* x, const float* W_r, const flo
                void* ws, size_t ws_bytes, void* stream);
 
 /*
+ * moe_router_masked - moe_router with experts taken out of the selection
+ * (aiany.app explainer, Step 9, probe 1: for each token, mask the routed
+ * experts the router wanted most and route among the rest; probe 2, fewer
+ * picks, is moe_router with a smaller cfg->k).
+ *   allow      [N] uint8 HOST array, nullable: experts with allow[e] == 0 are
+ *              never selected
+ *   mask_top   per token, its mask_top highest keys among the allowed experts
+ *              (key descending, index ascending) are excluded as well; 0 = none
+ * The scores (p or s, and so the gates of the experts that are selected) are
+ * those of the unmasked router; group scores and the top-k use only the keys
+ * left.  Other arguments as moe_router.  Returns MOE_ERR_INVALID_ARG unless
+ * every group keeps group_topn + mask_top allowed experts and the kept groups
+ * hold k + mask_top of them (so every token still finds k experts).
+ */
+int moe_router_masked(const moe_config* cfg, const void* x, const float* W_r, const float* b,
+                      const uint8_t* allow, int32_t mask_top, int32_t* topk_idx,
+                      float* topk_gate, float* scores, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * moe_bias_update - auxiliary-loss-free balancing step (grasp.study lesson,
+ * 3.2: each expert's selection bias is nudged after a batch, up when the
+ * expert was underloaded and down when it was overloaded).
+ *   b          [N] fp32 device, updated in place:
+ *              b[i] += gamma if N*counts[i] < T*k, -= gamma if greater, else kept
+ *   counts     [N] int32 device: the batch's selections per expert (moe_permute
+ *              or moe_forward's counts_out), T*k of them in total (cfg->T, cfg->k)
+ *   gamma      step, finite and >= 0
+ * Needs no workspace.  Enqueued on `stream`.
+ */
+int moe_bias_update(const moe_config* cfg, float* b, const int32_t* counts, float gamma,
+                    void* stream);
+
+/*
  * moe_permute - stable counting sort of the T*k (token, expert) slots into
  * expert-contiguous rows (the bincount and per-expert row lists of the
  * reference forward excerpt on open-model-atlas, done on the device).

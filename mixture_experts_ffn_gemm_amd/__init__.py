@@ -9,6 +9,8 @@ raises ImportError, and the library itself needs a GPU to run.
 """
 from __future__ import annotations
 
+import ctypes
+
 import torch
 
 from . import _lib
@@ -86,6 +88,45 @@ def router(cfg: MoeConfig, x, W_r, b=None, topk_idx=None, topk_gate=None, scores
         _p(scores, "scores", (torch.float32,), T * N, optional=True), wsp, wsn, _stream(stream))
     _lib.check("moe_router", st)
     return (topk_idx, topk_gate, scores) if want_scores else (topk_idx, topk_gate)
+
+
+def router_masked(cfg: MoeConfig, x, W_r, b=None, allow=None, mask_top=0, want_scores=False,
+                  ws=None, stream=None):
+    """moe_router_masked: the router with experts out of the selection.  ``allow``
+    is a host sequence of N truthy values (None = all allowed); ``mask_top``
+    removes each token's best remaining experts.  Returns (topk_idx, topk_gate[,
+    scores])."""
+    T, d, N, k = cfg.T, cfg.d, cfg.n_routed, cfg.k
+    dev = x.device
+    topk_idx = torch.empty((T, k), dtype=torch.int32, device=dev)
+    topk_gate = torch.empty((T, k), dtype=torch.float32, device=dev)
+    scores = torch.empty((T, N), dtype=torch.float32, device=dev) if want_scores else None
+    allow_buf = None
+    if allow is not None:
+        allow = [1 if a else 0 for a in allow]
+        if len(allow) != N:
+            raise ValueError(f"allow has {len(allow)} entries, expected {N}")
+        allow_buf = (ctypes.c_uint8 * N)(*allow)
+    wsp, wsn = _ws(cfg, ws, dev)
+    st = _lib.LIB.moe_router_masked(
+        cfg, _p(x, "x", _ACT[cfg.act_dtype], T * d), _p(W_r, "W_r", (torch.float32,), N * d),
+        _p(b, "b", (torch.float32,), N, optional=True),
+        ctypes.cast(allow_buf, ctypes.c_void_p) if allow_buf is not None else None, int(mask_top),
+        _p(topk_idx, "topk_idx", (torch.int32,), T * k), _p(topk_gate, "topk_gate", (torch.float32,), T * k),
+        _p(scores, "scores", (torch.float32,), T * N, optional=True), wsp, wsn, _stream(stream))
+    _lib.check("moe_router_masked", st)
+    return (topk_idx, topk_gate, scores) if want_scores else (topk_idx, topk_gate)
+
+
+def bias_update(cfg: MoeConfig, b, counts, gamma: float, stream=None):
+    """moe_bias_update: b [N] fp32 (device, in place) moves by gamma towards
+    balance given the batch's counts [N] int32."""
+    N = cfg.n_routed
+    st = _lib.LIB.moe_bias_update(cfg, _p(b, "b", (torch.float32,), N),
+                                  _p(counts, "counts", (torch.int32,), N), float(gamma),
+                                  _stream(stream))
+    _lib.check("moe_bias_update", st)
+    return b
 
 
 def permute(cfg: MoeConfig, topk_idx, x=None, want_x_perm=False, ws=None, stream=None):

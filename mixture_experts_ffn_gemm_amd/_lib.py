@@ -20,8 +20,8 @@ GATES = {"softmax": 0, "sigmoid": 1}
 
 # every symbol include/moe.h declares
 EXPORTS = ["moe_status_string", "moe_last_error", "moe_version", "moe_workspace_size",
-           "moe_router", "moe_permute", "moe_expert_ffn", "moe_combine", "moe_forward",
-           "moe_forward_timed"]
+           "moe_router", "moe_router_masked", "moe_bias_update", "moe_permute", "moe_expert_ffn",
+           "moe_combine", "moe_forward", "moe_forward_timed"]
 
 
 class MoeConfig(ctypes.Structure):
@@ -40,7 +40,7 @@ class MoeError(RuntimeError):
 
 def _load():
     if not os.path.exists(LIB_PATH):
-        raise ImportError(f"{LIB_PATH} is not built; run `python -m mixture_experts_ffn_gemm_amd.build`")
+        raise ImportError(f"{LIB_PATH} is not built; run `python mixture_experts_ffn_gemm_amd/build.py`")
     lib = ctypes.CDLL(LIB_PATH)
     P = c_void_p
     lib.moe_status_string.restype = c_char_p
@@ -53,6 +53,11 @@ def _load():
     lib.moe_workspace_size.argtypes = [POINTER(MoeConfig)]
     lib.moe_router.restype = ctypes.c_int
     lib.moe_router.argtypes = [POINTER(MoeConfig), P, P, P, P, P, P, P, c_size_t, P]
+    lib.moe_router_masked.restype = ctypes.c_int
+    lib.moe_router_masked.argtypes = [POINTER(MoeConfig), P, P, P, P, c_int32, P, P, P, P, c_size_t,
+                                      P]
+    lib.moe_bias_update.restype = ctypes.c_int
+    lib.moe_bias_update.argtypes = [POINTER(MoeConfig), P, P, c_float, P]
     lib.moe_permute.restype = ctypes.c_int
     lib.moe_permute.argtypes = [POINTER(MoeConfig), P, P, P, P, P, P, P, P, c_size_t, P]
     lib.moe_expert_ffn.restype = ctypes.c_int

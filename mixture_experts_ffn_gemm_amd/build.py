@@ -1,6 +1,6 @@
 """Build libmoe.so (gfx950) from csrc/ with hipcc, in-tree.
 
-    python -m mixture_experts_ffn_gemm_amd.build        # or build() from Python
+    python mixture_experts_ffn_gemm_amd/build.py        # or __graft_entry__.build()
 
 Every .hip / .cpp file under csrc/ is compiled to an object in _build/ at the
 repository root and linked into mixture_experts_ffn_gemm_amd/libmoe.so.

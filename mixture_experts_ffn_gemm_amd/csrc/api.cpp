@@ -135,7 +135,8 @@ P* at(void* ws, size_t off) {
 }
 
 int run_router(const moe_config* c, const void* x, const float* W_r, const float* b,
-               int32_t* idx, float* gate, float* scores, void* ws, hipStream_t s) {
+               int32_t* idx, float* gate, float* scores, void* ws, hipStream_t s,
+               const ExpertMask* mask = nullptr) {
   const Layout L = make_layout(*c);
   float* z = at<float>(ws, L.z);
   int nsplit = 1;
@@ -147,7 +148,35 @@ int run_router(const moe_config* c, const void* x, const float* W_r, const float
     MOE_HIP_CHECK(launch_router_logits_simt(false, x, W_r, z, c->T, c->d, c->n_routed, s));
   }
   MOE_HIP_CHECK(launch_router_select(z, nsplit, b, c->T, c->n_routed, c->k, c->n_groups, c->topk_groups,
-                                     c->group_topn, c->gate, c->route_scale, idx, gate, scores, s));
+                                     c->group_topn, c->gate, c->route_scale, idx, gate, scores, s,
+                                     mask));
+  return MOE_OK;
+}
+
+// Host check that every token still finds k experts after the exclusions:
+// every group keeps group_topn + mask_top allowed experts and the kept groups
+// hold k + mask_top of them.
+int build_mask(const moe_config* c, const uint8_t* allow, int32_t mask_top, ExpertMask* m) {
+  *m = ExpertMask{};
+  if (mask_top < 0) return fail(MOE_ERR_INVALID_ARG, "mask_top must be >= 0");
+  const int N = c->n_routed, G = c->n_groups, gs = N / G;
+  int min_group = gs;
+  for (int g = 0; g < G; ++g) {
+    int n = 0;
+    for (int e = g * gs; e < (g + 1) * gs; ++e)
+      if (!allow || allow[e]) {
+        ++n;
+        m->allow[e >> 6] |= 1ull << (e & 63);
+      }
+    min_group = n < min_group ? n : min_group;
+  }
+  m->any = allow ? 1 : 0;
+  m->top = mask_top;
+  if (G > 1 && min_group < c->group_topn + mask_top)
+    return fail(MOE_ERR_INVALID_ARG,
+                "every group must keep group_topn + mask_top allowed experts");
+  if ((int64_t)min_group * (G > 1 ? c->topk_groups : 1) < (int64_t)c->k + mask_top)
+    return fail(MOE_ERR_INVALID_ARG, "fewer than k experts would remain after the exclusions");
   return MOE_OK;
 }
 
@@ -249,6 +278,34 @@ int moe_router(const moe_config* cfg, const void* x, const float* W_r, const flo
     return fail(MOE_ERR_INVALID_ARG, "x, W_r, topk_idx and topk_gate must be non-NULL");
   if ((st = check_ws(cfg, ws, ws_bytes))) return st;
   return run_router(cfg, x, W_r, b, topk_idx, topk_gate, scores, ws, (hipStream_t)stream);
+}
+
+int moe_router_masked(const moe_config* cfg, const void* x, const float* W_r, const float* b,
+                      const uint8_t* allow, int32_t mask_top, int32_t* topk_idx, float* topk_gate,
+                      float* scores, void* ws, size_t ws_bytes, void* stream) {
+  g_err.clear();
+  int st = check_config(cfg);
+  if (st) return st;
+  ExpertMask m;
+  if ((st = build_mask(cfg, allow, mask_top, &m))) return st;
+  if (cfg->T == 0) return MOE_OK;
+  if (!x || !W_r || !topk_idx || !topk_gate)
+    return fail(MOE_ERR_INVALID_ARG, "x, W_r, topk_idx and topk_gate must be non-NULL");
+  if ((st = check_ws(cfg, ws, ws_bytes))) return st;
+  return run_router(cfg, x, W_r, b, topk_idx, topk_gate, scores, ws, (hipStream_t)stream, &m);
+}
+
+int moe_bias_update(const moe_config* cfg, float* b, const int32_t* counts, float gamma,
+                    void* stream) {
+  g_err.clear();
+  int st = check_config(cfg);
+  if (st) return st;
+  if (!b || !counts) return fail(MOE_ERR_INVALID_ARG, "b and counts must be non-NULL");
+  if (!std::isfinite(gamma) || gamma < 0.f)
+    return fail(MOE_ERR_INVALID_ARG, "gamma must be finite and >= 0");
+  MOE_HIP_CHECK(launch_bias_update(b, counts, cfg->n_routed, cfg->T * (int64_t)cfg->k, gamma,
+                                   (hipStream_t)stream));
+  return MOE_OK;
 }
 
 int moe_permute(const moe_config* cfg, const int32_t* topk_idx, const void* x, int32_t* counts,

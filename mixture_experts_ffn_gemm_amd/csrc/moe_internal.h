@@ -45,10 +45,20 @@ hipError_t launch_router_logits_mfma(const bf16_t* x, const float* W_r, float* z
                                      int d, int N, int nsplit, hipStream_t stream);
 
 // Scores, group-limited top-k and gates from z (the sum of nsplit partials).
+// Experts out of the selection: allow bit e of word e/64 (when `any`), then
+// each token's `top` best remaining keys.
+struct ExpertMask {
+  uint64_t allow[4];
+  int any;
+  int top;
+};
 hipError_t launch_router_select(const float* z, int nsplit, const float* b, int64_t T, int N, int k,
                                 int n_groups, int topk_groups, int group_topn, int gate,
                                 float route_scale, int32_t* idx, float* gates, float* scores,
-                                hipStream_t stream);
+                                hipStream_t stream, const ExpertMask* mask = nullptr);
+// b[i] += gamma * sign(slots - N * counts[i])
+hipError_t launch_bias_update(float* b, const int32_t* counts, int N, int64_t slots, float gamma,
+                              hipStream_t stream);
 
 // Counting-sort permutation of the S = T*k slots.
 constexpr int kPermChunk = 256;  // slots per wavefront chunk

@@ -266,7 +266,7 @@ __device__ __forceinline__ int unpack_idx(uint64_t p) {
 
 __global__ __launch_bounds__(256) void router_select_kernel(
     const float* __restrict__ z, int nsplit, const float* __restrict__ b, int64_t T, int N, int k,
-    int n_groups, int topk_groups, int group_topn, int gate, float route_scale,
+    int n_groups, int topk_groups, int group_topn, int gate, float route_scale, ExpertMask mask,
     int32_t* __restrict__ out_idx, float* __restrict__ out_gate, float* __restrict__ scores) {
   const int lane = lane_id();
   const int64_t t = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
@@ -325,6 +325,32 @@ __global__ __launch_bounds__(256) void router_select_kernel(
 #pragma unroll
   for (int j = 0; j < kSelPerLane; ++j)
     if (!ok[j]) key[j] = NEG_INF;
+
+  // ---- experts taken out of the selection (aiany.app explainer, Step 9,
+  // probe 1): a fixed set, then each token's mask_top highest remaining keys
+  // (same order as the top-k: key descending, index ascending).  The scores
+  // written above are unchanged.
+  if (mask.any) {
+#pragma unroll
+    for (int j = 0; j < kSelPerLane; ++j)
+      if (!((mask.allow[j] >> lane) & 1ull)) key[j] = NEG_INF;
+  }
+  for (int r = 0; r < mask.top; ++r) {
+    uint64_t best = 0;
+#pragma unroll
+    for (int j = 0; j < kSelPerLane; ++j)
+      if (key[j] != NEG_INF) {
+        const uint64_t p = pack_key(key[j], lane + 64 * j);
+        best = p > best ? p : best;
+      }
+    best = wave_max_u64(best);
+    const int e_sel = unpack_idx(best);
+    if ((e_sel & 63) == lane) {
+#pragma unroll
+      for (int j = 0; j < kSelPerLane; ++j)
+        if (j == (e_sel >> 6)) key[j] = NEG_INF;
+    }
+  }
 
   // ---- group limit: score = sum of the group_topn largest keys of the group
   if (n_groups > 1) {
@@ -405,11 +431,30 @@ __global__ __launch_bounds__(256) void router_select_kernel(
 hipError_t launch_router_select(const float* z, int nsplit, const float* b, int64_t T, int N, int k,
                                 int n_groups, int topk_groups, int group_topn, int gate,
                                 float route_scale, int32_t* idx, float* gates, float* scores,
-                                hipStream_t stream) {
+                                hipStream_t stream, const ExpertMask* mask) {
   const unsigned blocks = (unsigned)cdiv(T, 4);
+  const ExpertMask m = mask ? *mask : ExpertMask{};
   router_select_kernel<<<blocks, 256, 0, stream>>>(z, nsplit, b, T, N, k, n_groups, topk_groups,
-                                                   group_topn, gate, route_scale, idx, gates,
+                                                   group_topn, gate, route_scale, m, idx, gates,
                                                    scores);
+  return hipGetLastError();
+}
+
+// Auxiliary-loss-free balancing step (grasp.study lesson, 3.2): expert i's
+// bias moves by gamma towards balance, up when its load is below the mean
+// slots/N and down when above; the comparison N*load_i vs slots is exact.
+__global__ void bias_update_kernel(float* __restrict__ b, const int32_t* __restrict__ counts,
+                                   int N, int64_t slots, float gamma) {
+  const int i = (int)blockIdx.x * 256 + threadIdx.x;
+  if (i >= N) return;
+  const int64_t load = (int64_t)counts[i] * N;
+  if (load < slots) b[i] = b[i] + gamma;
+  else if (load > slots) b[i] = b[i] - gamma;
+}
+
+hipError_t launch_bias_update(float* b, const int32_t* counts, int N, int64_t slots, float gamma,
+                              hipStream_t stream) {
+  bias_update_kernel<<<(unsigned)cdiv(N, 256), 256, 0, stream>>>(b, counts, N, slots, gamma);
   return hipGetLastError();
 }
 

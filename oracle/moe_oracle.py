@@ -217,8 +217,8 @@ def route(cfg, x64: np.ndarray, wr64: np.ndarray, b=None, allow=None, mask_top: 
     idx, kmargin = topk_select(key_sel, allowed, cfg.k)
     gates = gate_values(cfg.gate, cfg.route_scale, value, idx)
     counts = np.bincount(idx.ravel(), minlength=cfg.n_routed)
-    return dict(z=z, value=value, key=key, allowed=allowed, group_scores=gscore,
-                idx=idx, gates=gates, counts=counts,
+    return dict(z=z, value=value, key=key, key_sel=key_sel, allowed=allowed,
+                group_scores=gscore, idx=idx, gates=gates, counts=counts,
                 margin=np.minimum(np.minimum(kmargin, gmargin), mmargin),
                 kmargin=kmargin, gmargin=gmargin, mmargin=mmargin)
 

@@ -72,8 +72,11 @@ def check_routing(cfg, r, idx_gpu: np.ndarray, gate_gpu: np.ndarray, gate_tol=2e
     assert np.all(np.diff(sg, axis=1) > 0)
     # near ties: every GPU pick must have a key within TIE of the k-th key and
     # lie in a group whose score is within TIE of the last kept group
-    key = r["key"]
+    key = r.get("key_sel", r["key"])  # keys left after any expert exclusion
+    mmargin = r.get("mmargin", np.full(T, np.inf))
     for t in np.nonzero(near & ~same)[0]:
+        if mmargin[t] < TIE:  # the excluded set itself is inside the tie window
+            continue
         kth = np.sort(key[t][r["allowed"][t]])[::-1][k - 1]
         assert np.all(key[t][idx_gpu[t]] >= kth - TIE), t
         if cfg.n_groups > 1:

@@ -89,3 +89,32 @@ def test_empty_batch_is_a_no_op(m):
     c.T, c.d = 0, 7168
     assert m._lib.LIB.moe_router(c, None, None, None, None, None, None, None, 0, None) == 0
     assert m._lib.LIB.moe_combine(c, None, None, None, None, None, None, None) == 0
+
+
+def test_router_masked_rejects_exclusions_that_leave_too_few(m):
+    L = m._lib.LIB
+    c = m.config_from(datagen.get_config("deepseekmoe_2b"))  # 63 experts, k = 7, ungrouped
+    allow = (ctypes.c_uint8 * 63)(*([1] * 8 + [0] * 55))     # 8 allowed experts
+    p = 0x1000
+    # 8 allowed - mask_top 2 < k = 7
+    assert L.moe_router_masked(c, p, p, None, ctypes.cast(allow, ctypes.c_void_p), 2, p, p, None,
+                               None, 0, None) == -1
+    assert "fewer than k" in m.last_error()
+    assert L.moe_router_masked(c, p, p, None, None, -1, p, p, None, None, 0, None) == -1
+    v3 = m.config_from(datagen.get_config("v3_prefill"))    # 8 groups of 32, top-2 group score
+    allow = (ctypes.c_uint8 * 256)(*([1] * 224 + [0] * 30 + [1] * 2))  # last group keeps 2
+    assert L.moe_router_masked(v3, p, p, None, ctypes.cast(allow, ctypes.c_void_p), 1, p, p, None,
+                               None, 0, None) == -1
+    assert "group_topn + mask_top" in m.last_error()
+    # valid exclusions with no workspace reach the workspace check (nothing is launched)
+    assert L.moe_router_masked(v3, p, p, None, None, 8, p, p, None, None, 0, None) == -3
+
+
+def test_bias_update_argument_checks(m):
+    L = m._lib.LIB
+    c = m.config_from(datagen.get_config("v3_prefill"))
+    p = 0x1000
+    assert L.moe_bias_update(c, None, p, 0.001, None) == -1
+    assert L.moe_bias_update(c, p, None, 0.001, None) == -1
+    assert L.moe_bias_update(c, p, p, float("nan"), None) == -1
+    assert L.moe_bias_update(c, p, p, -1.0, None) == -1

@@ -67,6 +67,72 @@ def test_router_full_size(lib, name):
         assert np.array_equal(counts, r["counts"])
 
 
+@pytest.mark.parametrize("name,mask_top,drop_every", [
+    ("deepseekmoe_2b", 1, 0), ("deepseekmoe_2b", 3, 5), ("v3_prefill", 2, 0), ("v3_prefill", 4, 7)])
+def test_router_masked(lib, name, mask_top, drop_every):
+    """Probe 1 (each token's mask_top favourite experts masked) and a fixed set
+    of excluded experts (every drop_every-th), against the oracle's router with
+    the same exclusions; the scores are those of the unmasked router."""
+    cfg = datagen.get_config(name, T=4096 if name == "deepseekmoe_2b" else 2048)
+    allow = None
+    if drop_every:
+        allow = np.ones(cfg.n_routed, bool)
+        allow[::drop_every] = False
+    say(f"[router-masked] {name} T={cfg.T} mask_top={mask_top} excluded={0 if allow is None else int((~allow).sum())}")
+    inp = datagen.MoEInputs(cfg)
+    x = inp.x()
+    r = oracle.route(cfg, oracle.widen(x, cfg.act_dtype), inp.router_w().astype(np.float64),
+                     inp.router_b(), allow=allow, mask_top=mask_top)
+    c = lib.config_from(cfg)
+    dev = torch.device("cuda")
+    b = None if inp.router_b() is None else to_torch(inp.router_b(), dev)
+    idx, gate, scores = lib.router_masked(c, to_torch(x, dev), to_torch(inp.router_w(), dev), b,
+                                          allow=None if allow is None else allow.tolist(),
+                                          mask_top=mask_top, want_scores=True)
+    torch.cuda.synchronize()
+    idx_np = idx.cpu().numpy()
+    near, order = check_routing(cfg, r, idx_np, gate.cpu().numpy())
+    if allow is not None:
+        assert allow[idx_np].all()
+    # no token picks one of its own mask_top favourites among the allowed experts
+    fav_key = np.where(allow[None, :] if allow is not None else True, r["key"], -np.inf)
+    fav = np.argsort(-fav_key, axis=1, kind="stable")[:, :mask_top]
+    clean = r["mmargin"] >= TIE
+    assert not (fav[clean][:, :, None] == idx_np[clean][:, None, :]).any()
+    s_err = np.max(np.abs(scores.cpu().numpy() - r["value"]) / np.maximum(r["value"], 1e-6))
+    say(f"   near-ties {near}, order diffs {order}, score rel err {s_err:.2e}")
+    assert s_err < 2e-5
+
+
+def test_bias_update_bit_exact(lib):
+    """The aux-loss-free step on the GPU equals the oracle's bit for bit, over
+    loads below, at and above the mean, applied repeatedly."""
+    cfg = datagen.get_config("v3_prefill", T=1000)
+    c = lib.config_from(cfg)
+    rng = np.random.default_rng(31)
+    slots = cfg.T * cfg.k  # mean load 31.25: no exact ties; add a config with exact ties below
+    b = rng.uniform(-0.05, 0.05, cfg.n_routed).astype(np.float32)
+    bd = torch.from_numpy(b.copy()).cuda()
+    for it in range(5):
+        counts = rng.integers(0, 64, cfg.n_routed).astype(np.int32)
+        lib.bias_update(c, bd, torch.from_numpy(counts).cuda(), 1e-3)
+        b = oracle.bias_update(b, counts, slots, 1e-3)
+    torch.cuda.synchronize()
+    assert np.array_equal(bd.cpu().numpy().view(np.uint32), b.view(np.uint32))
+    # mean exactly 32: loads of 32 leave the bias unchanged
+    cfg2 = datagen.get_config("v3_prefill", T=1024)
+    c2 = lib.config_from(cfg2)
+    counts = np.full(cfg2.n_routed, 32, np.int32)
+    counts[:8] = [0, 31, 33, 64, 32, 1, 63, 32]
+    b2 = rng.uniform(-1, 1, cfg2.n_routed).astype(np.float32)
+    bd2 = torch.from_numpy(b2.copy()).cuda()
+    lib.bias_update(c2, bd2, torch.from_numpy(counts).cuda(), 0.25)
+    torch.cuda.synchronize()
+    want = oracle.bias_update(b2, counts, cfg2.T * cfg2.k, 0.25)
+    assert np.array_equal(bd2.cpu().numpy().view(np.uint32), want.view(np.uint32))
+    assert np.array_equal(want[8:], b2[8:])
+
+
 def test_router_zero_weights_tie_break(lib):
     """All keys equal: experts 0..k-1 (groups 0..3 for the V3 router)."""
     for name in ("gshard_fp32", "v3_prefill"):
