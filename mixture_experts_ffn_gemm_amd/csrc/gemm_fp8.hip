@@ -154,10 +154,15 @@ __device__ __forceinline__ void fp8_tile(const GroupedGemmArgs& args, const Tile
   }
 }
 
+// The down projection's tiles are short (64 columns x K = I): a ring of 4
+// k-blocks within 128 VGPRs gives four resident workgroups per CU, whose
+// start-up latencies (tile lookup, row indices, activations) then overlap
+// each other's weight streams.  The up projection streams two matrices over
+// K = d per tile and keeps 2 workgroups per CU with a ring of 4.
 template <bool SWIGLU>
-__global__ __launch_bounds__(256) void gemm_fp8_small_kernel(GroupedGemmArgs args) {
+__global__ __launch_bounds__(256, SWIGLU ? 1 : 4) void gemm_fp8_small_kernel(GroupedGemmArgs args) {
   constexpr int BM = 64, BN = 64;
-  constexpr int PF = SWIGLU ? 4 : 8;
+  constexpr int PF = 4;
   __shared__ int s_ts[kMaxGroups + 1];
   __shared__ int s_scratch[4];
   __shared__ int s_info[1];
