@@ -126,7 +126,7 @@ def time_next_rows(moe, c, dev, counts, events: HipEvents, stream, reps=20):
     return out
 
 
-def run_workload(name, steps, warmup, events: HipEvents, extra=False):
+def run_workload(name, steps, warmup, events: HipEvents, extra=False, one_stream=False):
     import torch
     import datagen
     from datagen.device import upload
@@ -142,7 +142,7 @@ def run_workload(name, steps, warmup, events: HipEvents, extra=False):
     out = torch.empty((cfg.T, cfg.d), dtype=torch.float32, device="cuda")
     counts = torch.empty(cfg.n_routed, dtype=torch.int32, device="cuda")
     main = torch.cuda.current_stream()
-    side = torch.cuda.Stream()
+    side = main if one_stream else torch.cuda.Stream()
     L = moe._lib.LIB
     ex, sh = dev["experts"], dev["shared"] or {}
     P = lambda t: None if t is None else t.data_ptr()
@@ -366,6 +366,8 @@ def main():
     ap.add_argument("--workload", default="v3_prefill")
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--one-stream", action="store_true",
+                    help="no side stream: the shared expert runs inside the routed GEMMs (bf16, S=1)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="launch a known-size copy first (scale for PMC byte counters)")
     args = ap.parse_args()
@@ -379,7 +381,8 @@ def main():
     events = HipEvents()
     if args.copy_calibration:
         copy_calibration()
-    r = run_workload(args.workload, args.steps, args.warmup, events, extra=True)
+    r = run_workload(args.workload, args.steps, args.warmup, events, extra=True,
+                     one_stream=args.one_stream)
     cfg = r["cfg"]
     value = cfg.T * args.steps / r["elapsed"]
     flops = cfg.flops_per_token() * cfg.T

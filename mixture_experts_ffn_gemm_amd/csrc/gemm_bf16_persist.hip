@@ -17,12 +17,20 @@
 // from the device offsets in LDS; the host never waits for the counts.
 //
 // Workgroup: 256 threads = 4 wavefronts, one per SIMD.  Wave w owns the
-// 32-row blocks w/2, w/2+2, .. (interleaved, so a partly filled tile still
-// spreads its MFMAs over all four SIMDs) and columns 128*(w%2) .. +128 of the
-// tile, as 4 x 4 tiles of v_mfma_f32_32x32x16_bf16 with the weight fragment
-// as the first operand, so each lane accumulates 4 runs of 4 consecutive
-// output columns of one row (256 fp32 accumulators in the AGPRs).  A lane pair (l, l+32) trades halves
-// with v_permlane32_swap in the epilogue and each lane stores 16 bytes.
+// 32-row blocks w/2, w/2+2, .. and columns 128*(w%2) .. +128 of the tile, as
+// 4 x 4 tiles of v_mfma_f32_32x32x16_bf16 with the weight fragment as the
+// first operand, so each lane accumulates 4 runs of 4 consecutive output
+// columns of one row (256 fp32 accumulators in the AGPRs).  A lane pair
+// (l, l+32) trades halves with v_permlane32_swap in the epilogue and each lane
+// stores 16 bytes.
+//
+// Every tile does all of its MFMAs, also past an expert's last row (those
+// rows repeat the last row and are not stored): tiles of equal cost keep the
+// workgroups of an XCD in step, so the panels they share are still in L2 when
+// each of them reads them.  Skipping the MFMAs of a partly filled tile made
+// such tiles finish early, the workgroups drifted apart and the routed up
+// projection of the V3-shaped layer read 37 GB past L2 instead of 21 GB and
+// ran 10% slower.
 //
 // Pipeline.  K is staged BK at a time through NS LDS stages by direct
 // global->LDS loads (global_load_lds_dwordx4).  A "step" is one BK slice of one
@@ -34,8 +42,7 @@
 // last k-step's MFMAs.  The gathered row indices of the tile after next are
 // fetched into LDS by a direct load too, so no load result is ever waited for
 // in registers.  LDS rows hold BK bf16 of one matrix row; their 16-byte chunks
-// are XOR-swizzled so the fragment reads are free of bank conflicts.  A wave
-// skips the MFMAs of its 32-row blocks past the expert's rows.
+// are XOR-swizzled so the fragment reads are free of bank conflicts.
 #include "grouped_sched.h"
 #include "moe_internal.h"
 
@@ -106,14 +113,11 @@ __device__ __forceinline__ void read_frags(const char* stage, int ks, int wm, in
   }
 }
 
-// The four MFMAs of row block i of one k-step (skipped past the wave's rows).
-template <int NB>
+// The four MFMAs of row block i of one k-step.
 __device__ __forceinline__ void mfma_row(int i, const Frags& f, f32x16_t (&acc)[MB][NT]) {
-  if (i < NB) {
 #pragma unroll
-    for (int j = 0; j < NT; ++j)
-      acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.b[j], f.a[i], acc[i][j], 0, 0, 0);
-  }
+  for (int j = 0; j < NT; ++j)
+    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.b[j], f.a[i], acc[i][j], 0, 0, 0);
 }
 
 // Per-workgroup tile table in LDS.
@@ -242,8 +246,8 @@ __device__ __forceinline__ void advance(Issuer<BK, SWIGLU>& is, const GroupedGem
 // 8*q + 4*(l>>5) + 0..3 (q = 0..3) of each 32-column tile; after the swap
 // with lane l^32, lane l holds columns 16*p + 8*(l>>5) + 0..7 (p = 0, 1).
 template <bool SWIGLU>
-__device__ __forceinline__ void store_tile(const GroupedGemmArgs& a, const Tile& t, int nbw,
-                                           int wm, int wn, int lane, f32x16_t (&acc)[MB][NT]) {
+__device__ __forceinline__ void store_tile(const GroupedGemmArgs& a, const Tile& t, int wm,
+                                           int wn, int lane, f32x16_t (&acc)[MB][NT]) {
   constexpr int NJ = SWIGLU ? NT / 2 : NT;
   constexpr int WCOLS = SWIGLU ? 64 : 128;  // output columns per wave
   bf16_t* __restrict__ C = (bf16_t*)a.C;
@@ -251,7 +255,6 @@ __device__ __forceinline__ void store_tile(const GroupedGemmArgs& a, const Tile&
   const int64_t nrows = t.rend - t.row0;
 #pragma unroll
   for (int i = 0; i < MB; ++i) {
-    if (i >= nbw) break;
     const int m = (2 * i + wm) * 32 + (lane & 31);
     const bool row_ok = m < nrows;
     bf16_t* crow = C + (t.row0 + m) * a.Nout;
@@ -303,12 +306,12 @@ __device__ __forceinline__ void store_tile(const GroupedGemmArgs& a, const Tile&
   }
 }
 
-// The steps of one tile for a wave with NB valid 32-row blocks.  Step g of
+// The steps of one tile.  Step g of
 // the sequence reads stage g % NS; during it the loads of step g+NS-1 go into
 // stage (g-1) % NS, which every wave finished reading before barrier B(g).
 // B(g+1) follows this thread's wait for its loads of step g+1 and for all its
 // LDS reads: after it step g+1 has landed for every thread.
-template <int BK, int NS, bool SWIGLU, int NB>
+template <int BK, int NS, bool SWIGLU>
 __device__ __forceinline__ void run_tile(int& g, int nk, Issuer<BK, SWIGLU>& is,
                                          const GroupedGemmArgs& a, TileTab& tt, const Sched& sc,
                                          char (*st)[Geo<BK>::STAGE_BYTES], int wm, int wn, int wv,
@@ -335,7 +338,7 @@ __device__ __forceinline__ void run_tile(int& g, int nk, Issuer<BK, SWIGLU>& is,
           read_frags<BK, SWIGLU>(st[(g + 1) % NS], 0, wm, wn, lane, fn);
           __builtin_amdgcn_sched_barrier(0);
         }
-        mfma_row<NB>(i, fc, acc);
+        mfma_row(i, fc, acc);
         __builtin_amdgcn_sched_barrier(0);
         if (grp < GROUPS) {
           // spread the LOADS loads of step g+NS-1 over the groups before B(g+1)
@@ -350,20 +353,6 @@ __device__ __forceinline__ void run_tile(int& g, int nk, Issuer<BK, SWIGLU>& is,
       }
     }
   }
-}
-
-template <int BK, int NS, bool SWIGLU, int NB>
-__device__ __forceinline__ void run_tile_dispatch(int nbw, int& g, int nk, Issuer<BK, SWIGLU>& is,
-                                                  const GroupedGemmArgs& a, TileTab& tt,
-                                                  const Sched& sc,
-                                                  char (*st)[Geo<BK>::STAGE_BYTES], int wm, int wn,
-                                                  int wv, int lane, Frags (&f)[2],
-                                                  f32x16_t (&acc)[MB][NT]) {
-  if (nbw == NB || NB == 0)
-    run_tile<BK, NS, SWIGLU, NB>(g, nk, is, a, tt, sc, st, wm, wn, wv, lane, f, acc);
-  else if constexpr (NB > 0)
-    run_tile_dispatch<BK, NS, SWIGLU, NB - 1>(nbw, g, nk, is, a, tt, sc, st, wm, wn, wv, lane, f,
-                                              acc);
 }
 
 template <int BK, int NS, bool SWIGLU>
@@ -430,20 +419,14 @@ __global__ __launch_bounds__(NTHR, 1) void gemm_bf16_persist_kernel(GroupedGemmA
   int g = 0;
   for (int i = 0; i < sc.ntile; ++i) {
     if (i > 0) t = decode_tile(tt, sc.n_groups, sc.ntn, CN, sc.tile_id(i));
-    const int64_t nrows64 = t.rend - t.row0;
-    const int nrows = nrows64 < BM ? (int)nrows64 : BM;
-    // row block i of wave row wm is block 2i+wm of the tile
-    int nbw = (((nrows + 31) >> 5) - wm + 1) >> 1;
-    nbw = nbw < 0 ? 0 : (nbw > MB ? MB : nbw);
 #pragma unroll
     for (int r = 0; r < MB; ++r)
 #pragma unroll
       for (int c = 0; c < NT; ++c)
 #pragma unroll
         for (int e = 0; e < 16; ++e) acc[r][c][e] = 0.f;
-    run_tile_dispatch<BK, NS, SWIGLU, MB>(nbw, g, nk, is, args, tt, sc, st, wm, wn, wv, lane, f,
-                                          acc);
-    store_tile<SWIGLU>(args, t, nbw, wm, wn, lane, acc);
+    run_tile<BK, NS, SWIGLU>(g, nk, is, args, tt, sc, st, wm, wn, wv, lane, f, acc);
+    store_tile<SWIGLU>(args, t, wm, wn, lane, acc);
   }
   // no load may still be writing LDS when the workgroup ends
   wait_vm_lgkm<0>();
