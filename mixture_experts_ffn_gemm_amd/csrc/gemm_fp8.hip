@@ -6,25 +6,47 @@
 // scales): one fp32 scale per 128 x 128 block of the stored [Nout, K] weight
 // matrix.  The expert math is the routed-expert SwiGLU of the same page.
 //
-// Decode is bound by streaming each selected expert's weights once, so the
-// weights go straight from HBM to registers (no LDS): a tile is (expert,
-// 64 output columns, up to 64 rows); each wavefront owns 16 columns over the
-// whole K.  Per 64 values of K, lane (col = lane & 15, kg = lane >> 4) loads
-// 16 consecutive fp8 weights of its column and feeds them to two
-// v_mfma_f32_16x16x32_bf16 (8 each); the activation operand is loaded with the
-// same k assignment, so the pair of MFMAs sums exactly the 64 products.  The
-// partial sum of each 128-wide K block is scaled once by its block scale.
+// Decode is bound by streaming each selected expert's weights once.  A tile
+// is (expert, 64 output columns, up to 64 rows); each wavefront owns 16
+// columns over the whole K.  Per 64 values of K, lane (col = lane & 15,
+// kg = lane >> 4) holds 16 consecutive fp8 weights of its column and feeds
+// them to two v_mfma_f32_16x16x32_bf16 (8 each); the activation operand uses
+// the same k assignment, so the pair of MFMAs sums exactly the 64 products.
+// The partial sum of each 128-wide K block is scaled once by its block scale.
 // Rows are handled in chunks of 16 (the MFMA M); chunks past the expert's row
 // count are skipped.  Experts without rows own no tile and are never read.
+//
+// Streaming.  The weights go straight from HBM into a per-lane register ring
+// PF k-blocks deep; a k-block's weights are converted to bf16 before the ring
+// slot is refilled, so the compiler never copies a register a load is still
+// writing.  The activations (a few rows, L2-resident) are read once per
+// workgroup, not once per wavefront: each thread loads its 16-byte pieces
+// into a small register ring, writes them to one of two LDS slots a k-block
+// ahead, and one barrier per k-block publishes them.  Every load is issued
+// unconditionally (past the end it repeats the last k-block), so the code is
+// straight-line and the compiler's wait counts keep the whole ring in flight.
+// With activations read once per wavefront instead, the extra loads cost
+// 25-45% of the streaming rate.
+#include <type_traits>
+
 #include "grouped_sched.h"
 #include "moe_internal.h"
 
 namespace moe {
 
+namespace f8 {
+
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+// the block scales are wave-uniform: constant-address loads become scalar loads
+typedef __attribute__((address_space(4))) const float cfloat;
+
+constexpr int BM = 64, BN = 64;
+constexpr int NCMAX = BM / 16;          // 16-row chunks per tile
+constexpr int CHUNK_BYTES = 16 * 256;   // 16 rows x 128 bf16 of one k-block
+constexpr int SLOT_BYTES = NCMAX * CHUNK_BYTES;
 
 // 8 e4m3 codes (two dwords) -> 8 bf16, exactly (every e4m3 value is a bf16 value)
 __device__ __forceinline__ bf16x8_t fp8x8_to_bf16(uint32_t w0, uint32_t w1) {
@@ -35,39 +57,81 @@ __device__ __forceinline__ bf16x8_t fp8x8_to_bf16(uint32_t w0, uint32_t w1) {
   return bf16x8_t{p0[0], p0[1], p1[0], p1[1], p2[0], p2[1], p3[0], p3[1]};
 }
 
-// K loop + epilogue for NC valid 16-row chunks.  PF k-blocks (128 values of K)
-// of this lane's weights are kept in flight in a register ring.
+template <int P, int N, class F>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (P < N) {
+    f(std::integral_constant<int, P>{});
+    static_for<P + 1, N>(f);
+  }
+}
+
+// k-blocks of activations held in registers ahead of their LDS write: PF
+// (then the weights keep their full lead) within 16 x 16 bytes per lane.
+constexpr int ra_for(int nc, int pf) {
+  int r = pf;
+  while (r > 1 && r * nc > 16) r /= 2;
+  return r;
+}
+
 template <bool SWIGLU, int NC, int PF>
-__device__ __forceinline__ void fp8_tile(const GroupedGemmArgs& args, const TileCoord& tc,
-                                         int nrows) {
+__device__ __forceinline__ void tile(const GroupedGemmArgs& args, const TileCoord& tc, int nrows,
+                                     char* aring) {
   constexpr int NB = SWIGLU ? 2 : 1;
-  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int col = lane & 15, kg = lane >> 4;
-  const int K = args.K, Nout = args.Nout, KB = K / 128;
+  const int K = args.K, Nout = args.Nout, KB = K / 128;  // KB % PF == 0
   const int ncol0 = tc.n0 + wv * 16;
 
   const uint8_t* bp[NB];
-  const float* sp[NB];
+  cfloat* sp[NB];
   {
     int n = ncol0 + col;
     if (n > Nout - 1) n = Nout - 1;
     const int64_t boff = ((int64_t)tc.group * Nout + n) * K + kg * 16;
-    const int64_t soff = ((int64_t)tc.group * (Nout / 128) + (n >> 7)) * KB;
+    // the wave's 16 columns lie in one 128-column scale block: scalar loads
+    const int g = __builtin_amdgcn_readfirstlane(tc.group);
+    const int nb = __builtin_amdgcn_readfirstlane((ncol0 < Nout ? ncol0 : Nout - 1) >> 7);
+    const int64_t soff = ((int64_t)g * (Nout / 128) + nb) * KB;
     bp[0] = (const uint8_t*)args.B0 + boff;
-    sp[0] = args.S0 + soff;
+    sp[0] = (cfloat*)(args.S0 + soff);
     if (SWIGLU) {
       bp[NB - 1] = (const uint8_t*)args.B1 + boff;
-      sp[NB - 1] = args.S1 + soff;
+      sp[NB - 1] = (cfloat*)(args.S1 + soff);
     }
   }
-  const bf16_t* ap[NC];
+  // Activation staging: in chunk c, wave wv fills LDS rows 4wv .. 4wv+3 of
+  // a slot; lane l writes row 4wv + (l >> 4), 16-byte position l & 15, with
+  // the row's 16-byte piece (l & 15) ^ row (rows are 256 bytes; the XOR spreads
+  // the pieces of one fragment read over all banks).  A k-block's pieces are
+  // loaded into registers RA k-blocks ahead and written to LDS (two
+  // slots) one k-block ahead.
+  constexpr int RA = ra_for(NC, PF);
+  static_assert(PF % RA == 0, "the register ring of A must repeat within PF");
+  const char* asrc[NC];
+  const int rl = wv * 4 + (lane >> 4);
+  {
+    const int piece = (lane & 15) ^ rl;
 #pragma unroll
-  for (int c = 0; c < NC; ++c) {
-    int64_t r = tc.row0 + c * 16 + col;
-    if (r > tc.rend - 1) r = tc.rend - 1;
-    const int64_t src = args.row_index ? (int64_t)args.row_index[r] : r;
-    ap[c] = (const bf16_t*)args.A + src * K + kg * 16;
+    for (int c = 0; c < NC; ++c) {
+      int64_t r = tc.row0 + c * 16 + rl;
+      if (r > tc.rend - 1) r = tc.rend - 1;
+      const int64_t src = args.row_index ? (int64_t)args.row_index[r] : r;
+      asrc[c] = (const char*)args.A + src * (int64_t)K * 2 + piece * 16;
+    }
   }
+  u32x4_t areg[RA][NC];
+  auto load_a = [&](int s, int kb) {
+    const int kc = kb < KB ? kb : KB - 1;
+#pragma unroll
+    for (int c = 0; c < NC; ++c) areg[s][c] = *(const u32x4_t*)(asrc[c] + kc * 256);
+  };
+  char* const wr_base = aring + rl * 256 + (lane & 15) * 16;
+  auto write_a = [&](int s, int kb) {
+    char* dst = wr_base + (kb & 1) * SLOT_BYTES;
+#pragma unroll
+    for (int c = 0; c < NC; ++c) *(u32x4_t*)(dst + c * CHUNK_BYTES) = areg[s][c];
+  };
 
   f32x4_t acc[NB][NC];
 #pragma unroll
@@ -76,66 +140,76 @@ __device__ __forceinline__ void fp8_tile(const GroupedGemmArgs& args, const Tile
     for (int c = 0; c < NC; ++c) acc[m][c] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
   u32x4_t ring[PF][NB][2];
+  auto load_w = [&](int p, int kb) {
+    const int kp = kb < KB ? kb : KB - 1;
 #pragma unroll
-  for (int p = 0; p < PF; ++p)
-    if (p < KB) {
+    for (int m = 0; m < NB; ++m)
+#pragma unroll
+      for (int h = 0; h < 2; ++h) ring[p][m][h] = *(const u32x4_t*)(bp[m] + kp * 128 + h * 64);
+  };
+  // prologue: A(0) to LDS slot 0, A(1 .. RA) into the register ring, the
+  // weights of k-blocks 0 .. PF-1 in flight
+  load_a(0, 0);
+  write_a(0, 0);
+#pragma unroll
+  for (int j = 1; j <= RA; ++j) load_a(j % RA, j);
+#pragma unroll
+  for (int p = 0; p < PF; ++p) load_w(p, p);
+
+  // k-block kb: (1) its weights to bf16, freeing their ring slot for the
+  // weights of kb+PF; (2) a barrier after this thread's LDS writes of A(kb):
+  // A(kb) is complete in slot kb&1 and every wave has finished reading slot
+  // (kb+1)&1 (A(kb-1)); (3) A(kb+1) from registers into that slot and A(kb+1+RA)
+  // requested into the freed registers; (4) the MFMAs on A(kb) from LDS.
+  // Loads past the end repeat the last k-block.
+  const int lrow = col;  // MFMA A-operand row of this lane
+  for (int kb0 = 0; kb0 < KB; kb0 += PF) {
+    static_for<0, PF>([&](auto pc) {
+      constexpr int p = decltype(pc)::value;
+      constexpr int sa = (p + 1) % RA;  // register slot of A(kb+1), then of A(kb+1+RA)
+      const int kb = kb0 + p;
+      bf16x8_t wb[NB][2][2];
 #pragma unroll
       for (int m = 0; m < NB; ++m)
 #pragma unroll
-        for (int h = 0; h < 2; ++h) ring[p][m][h] = *(const u32x4_t*)(bp[m] + p * 128 + h * 64);
-    }
-
-  for (int kb0 = 0; kb0 < KB; kb0 += PF) {
-#pragma unroll
-    for (int p = 0; p < PF; ++p) {
-      const int kb = kb0 + p;
-      if (kb < KB) {
-        u32x4_t cur[NB][2];
-#pragma unroll
-        for (int m = 0; m < NB; ++m)
-#pragma unroll
-          for (int h = 0; h < 2; ++h) cur[m][h] = ring[p][m][h];
-        if (kb + PF < KB) {
-#pragma unroll
-          for (int m = 0; m < NB; ++m)
-#pragma unroll
-            for (int h = 0; h < 2; ++h)
-              ring[p][m][h] = *(const u32x4_t*)(bp[m] + (kb + PF) * 128 + h * 64);
-        }
-        float sc[NB];
-#pragma unroll
-        for (int m = 0; m < NB; ++m) sc[m] = sp[m][kb];
-        f32x4_t tmp[NB][NC];
-#pragma unroll
-        for (int m = 0; m < NB; ++m)
-#pragma unroll
-          for (int c = 0; c < NC; ++c) tmp[m][c] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
         for (int h = 0; h < 2; ++h) {
-          const int k0 = kb * 128 + h * 64;
-          bf16x8_t blo[NB], bhi[NB];
+          wb[m][h][0] = fp8x8_to_bf16(ring[p][m][h][0], ring[p][m][h][1]);
+          wb[m][h][1] = fp8x8_to_bf16(ring[p][m][h][2], ring[p][m][h][3]);
+        }
+      load_w(p, kb + PF);
+      __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): this thread's LDS writes
+      __builtin_amdgcn_s_barrier();
+      write_a(sa, kb + 1);
+      load_a(sa, kb + 1 + RA);
+      const char* slot = aring + (kb & 1) * SLOT_BYTES;
+      float sc[NB];
+#pragma unroll
+      for (int m = 0; m < NB; ++m) sc[m] = sp[m][kb];
+      f32x4_t tmp[NB][NC];
+#pragma unroll
+      for (int m = 0; m < NB; ++m)
+#pragma unroll
+        for (int c = 0; c < NC; ++c) tmp[m][c] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int q0 = h * 8 + kg * 2;
+#pragma unroll
+        for (int c = 0; c < NC; ++c) {
+          const char* rowp = slot + c * CHUNK_BYTES + lrow * 256;
+          const bf16x8_t alo = *(const bf16x8_t*)(rowp + ((q0 ^ lrow) << 4));
+          const bf16x8_t ahi = *(const bf16x8_t*)(rowp + (((q0 + 1) ^ lrow) << 4));
 #pragma unroll
           for (int m = 0; m < NB; ++m) {
-            blo[m] = fp8x8_to_bf16(cur[m][h][0], cur[m][h][1]);
-            bhi[m] = fp8x8_to_bf16(cur[m][h][2], cur[m][h][3]);
-          }
-#pragma unroll
-          for (int c = 0; c < NC; ++c) {
-            const bf16x8_t alo = *(const bf16x8_t*)(ap[c] + k0);
-            const bf16x8_t ahi = *(const bf16x8_t*)(ap[c] + k0 + 8);
-#pragma unroll
-            for (int m = 0; m < NB; ++m) {
-              tmp[m][c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(alo, blo[m], tmp[m][c], 0, 0, 0);
-              tmp[m][c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ahi, bhi[m], tmp[m][c], 0, 0, 0);
-            }
+            tmp[m][c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(alo, wb[m][h][0], tmp[m][c], 0, 0, 0);
+            tmp[m][c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ahi, wb[m][h][1], tmp[m][c], 0, 0, 0);
           }
         }
-#pragma unroll
-        for (int m = 0; m < NB; ++m)
-#pragma unroll
-          for (int c = 0; c < NC; ++c) acc[m][c] += tmp[m][c] * sc[m];
       }
-    }
+#pragma unroll
+      for (int m = 0; m < NB; ++m)
+#pragma unroll
+        for (int c = 0; c < NC; ++c) acc[m][c] += tmp[m][c] * sc[m];
+    });
   }
 
   bf16_t* __restrict__ C = (bf16_t*)args.C;
@@ -154,18 +228,16 @@ __device__ __forceinline__ void fp8_tile(const GroupedGemmArgs& args, const Tile
   }
 }
 
-// The down projection's tiles are short (64 columns x K = I): a ring of 4
-// k-blocks within 128 VGPRs gives four resident workgroups per CU, whose
-// start-up latencies (tile lookup, row indices, activations) then overlap
-// each other's weight streams.  The up projection streams two matrices over
-// K = d per tile and keeps 2 workgroups per CU with a ring of 4.
-template <bool SWIGLU>
-__global__ __launch_bounds__(256, SWIGLU ? 1 : 4) void gemm_fp8_small_kernel(GroupedGemmArgs args) {
-  constexpr int BM = 64, BN = 64;
-  constexpr int PF = 4;
-  __shared__ int s_ts[kMaxGroups + 1];
-  __shared__ int s_scratch[4];
-  __shared__ int s_info[1];
+// One workgroup per tile; PF = depth of the weight ring (K / 128 must be a
+// multiple of it), LB = workgroups per CU the registers are budgeted for.
+template <bool SWIGLU, int PF, int LB>
+__global__ __launch_bounds__(256, LB) void gemm_fp8_small_kernel(GroupedGemmArgs args) {
+  // one LDS object: the two activation slots, then the tile-lookup scratch
+  __shared__ __attribute__((aligned(1024))) char smem[2 * SLOT_BYTES + (kMaxGroups + 1 + 8) * 4];
+  char* aring = smem;
+  int* s_ts = (int*)(smem + 2 * SLOT_BYTES);
+  int* s_scratch = s_ts + kMaxGroups + 1;
+  int* s_info = s_scratch + 4;
   TileCoord tc;
   if (!grouped_tile_lookup<256>(args.offsets, args.n_groups, BM, BN, args.Nout, s_ts, s_scratch,
                                 s_info, &tc))
@@ -173,24 +245,36 @@ __global__ __launch_bounds__(256, SWIGLU ? 1 : 4) void gemm_fp8_small_kernel(Gro
   const int64_t nrows_ = tc.rend - tc.row0;
   const int nrows = nrows_ < BM ? (int)nrows_ : BM;
   switch ((nrows + 15) >> 4) {
-    case 1: fp8_tile<SWIGLU, 1, PF>(args, tc, nrows); break;
-    case 2: fp8_tile<SWIGLU, 2, PF>(args, tc, nrows); break;
-    case 3: fp8_tile<SWIGLU, 3, PF>(args, tc, nrows); break;
-    default: fp8_tile<SWIGLU, 4, PF>(args, tc, nrows); break;
+    case 1: tile<SWIGLU, 1, PF>(args, tc, nrows, aring); break;
+    case 2: tile<SWIGLU, 2, PF>(args, tc, nrows, aring); break;
+    case 3: tile<SWIGLU, 3, PF>(args, tc, nrows, aring); break;
+    default: tile<SWIGLU, 4, PF>(args, tc, nrows, aring); break;
   }
 }
 
+}  // namespace f8
+
+// Up: W1 and W3 streams, a ring of 4 k-blocks, two workgroups per CU.  Down:
+// one stream over a short K (= I), a ring of 2 k-blocks and four workgroups
+// per CU, whose start-up latencies (tile lookup, row indices) then overlap
+// each other's streams.  K / 128 not a multiple of the ring: a ring of 1.
 hipError_t launch_gemm_fp8_swiglu(const GroupedGemmArgs& a, hipStream_t s) {
-  const int64_t grid = grouped_grid(a.max_rows, a.n_groups, 64, 64, a.Nout);
+  const int64_t grid = grouped_grid(a.max_rows, a.n_groups, f8::BM, f8::BN, a.Nout);
   if (grid <= 0) return hipSuccess;
-  gemm_fp8_small_kernel<true><<<(unsigned)grid, 256, 0, s>>>(a);
+  if ((a.K / 128) % 4 == 0)
+    f8::gemm_fp8_small_kernel<true, 4, 2><<<(unsigned)grid, 256, 0, s>>>(a);
+  else
+    f8::gemm_fp8_small_kernel<true, 1, 2><<<(unsigned)grid, 256, 0, s>>>(a);
   return hipGetLastError();
 }
 
 hipError_t launch_gemm_fp8_store(const GroupedGemmArgs& a, hipStream_t s) {
-  const int64_t grid = grouped_grid(a.max_rows, a.n_groups, 64, 64, a.Nout);
+  const int64_t grid = grouped_grid(a.max_rows, a.n_groups, f8::BM, f8::BN, a.Nout);
   if (grid <= 0) return hipSuccess;
-  gemm_fp8_small_kernel<false><<<(unsigned)grid, 256, 0, s>>>(a);
+  if ((a.K / 128) % 2 == 0)
+    f8::gemm_fp8_small_kernel<false, 2, 4><<<(unsigned)grid, 256, 0, s>>>(a);
+  else
+    f8::gemm_fp8_small_kernel<false, 1, 4><<<(unsigned)grid, 256, 0, s>>>(a);
   return hipGetLastError();
 }
 

@@ -187,20 +187,23 @@ def _rows_and_offsets(counts):
     return off, int(off[-1])
 
 
-@pytest.mark.parametrize("wdt", ["f32", "bf16", "fp8", "bf16_small_k", "bf16_many_tiles"])
+@pytest.mark.parametrize("wdt", ["f32", "bf16", "fp8", "fp8_k384", "bf16_small_k", "bf16_many_tiles"])
 def test_expert_ffn_ragged_groups(lib, wdt):
     """Groups of 0, 1, tile-1, tile, tile+1 and several tiles of rows.
 
+    fp8 (d = 512, I = 384) and fp8_k384 (d = 384, I = 512): K / 128 of 4 and 3
+    for the up projection, 3 and 4 for the down projection, so each projection
+    runs both its deep weight ring and its one-deep fallback.
     bf16_small_k: K = 128 for both projections, the smallest K the bf16 path
     takes (four 32-deep steps per tile, as many as the pipeline has stages).
     bf16_many_tiles: more tiles than workgroups, so every persistent workgroup
     runs its pipeline across several tiles of different experts and fills."""
-    d, I = {"f32": (256, 512), "bf16_small_k": (128, 128)}.get(wdt, (512, 384))
+    d, I = {"f32": (256, 512), "bf16_small_k": (128, 128), "fp8_k384": (384, 512)}.get(wdt, (512, 384))
     counts = [0, 1, 127, 128, 129, 300, 0, 5, 64, 65]
     if wdt == "bf16_many_tiles":
         counts = [int(c) for c in np.random.default_rng(11).integers(0, 700, 72)]
         counts[:6] = [0, 1, 255, 256, 257, 699]
-    name = {"f32": "gshard_fp32", "fp8": "v3_decode"}.get(wdt, "deepseekmoe_2b")
+    name = {"f32": "gshard_fp32", "fp8": "v3_decode", "fp8_k384": "v3_decode"}.get(wdt, "deepseekmoe_2b")
     cfg = datagen.get_config(name, d=d, inter=I, n_routed=len(counts), k=1, n_groups=1,
                              topk_groups=1, T=sum(counts), n_shared=0)
     say(f"[expert_ffn] {wdt} d={d} I={I} counts={counts}")
