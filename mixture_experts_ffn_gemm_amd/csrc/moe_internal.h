@@ -43,6 +43,9 @@ hipError_t launch_router_logits_simt(bool x_bf16, const void* x, const float* W_
 int router_mfma_splits(int64_t T, int d, int N);
 hipError_t launch_router_logits_mfma(const bf16_t* x, const float* W_r, float* zpart, int64_t T,
                                      int d, int N, int nsplit, hipStream_t stream);
+// zpart[0] = the sum of the nsplit partials in split order (TN = T * N)
+hipError_t launch_router_sum_splits(float* zpart, int nsplit, int64_t TN, hipStream_t stream);
+constexpr int kRouterSelectSplits = 8;  // partials the selection adds itself
 
 // Scores, group-limited top-k and gates from z (the sum of nsplit partials).
 // Experts out of the selection: allow bit e of word e/64 (when `any`), then
@@ -62,6 +65,7 @@ hipError_t launch_bias_update(float* b, const int32_t* counts, int N, int64_t sl
 
 // Counting-sort permutation of the S = T*k slots.
 constexpr int kPermChunk = 256;  // slots per wavefront chunk
+constexpr int kPermIdBits = 8;   // expert ids are below 256
 hipError_t launch_permute(const int32_t* idx, int64_t T, int k, int N, int32_t* hist,
                           int32_t* base, int32_t* rank, int32_t* counts, int32_t* offsets,
                           int32_t* row_token, int32_t* slot_row, hipStream_t stream);

@@ -7,7 +7,8 @@
 // counting sort on the device (no host round trip):
 //   1. hist:    one wavefront per chunk of 256 slots counts its experts in LDS
 //               and records each slot's rank among equal experts of the chunk
-//               (ballot + popcount, in slot order);
+//               (64 slots at a time: one ballot per bit of the expert id gives
+//               each lane the lanes of its expert; popcounts give the rank);
 //   2. scan:    one block per expert scans the chunk counts -> per-chunk base
 //               and the expert's total;
 //   3. scatter: row = offset[e] + base[chunk][e] + rank; row_token / slot_row.
@@ -33,22 +34,23 @@ __global__ __launch_bounds__(256) void permute_hist_kernel(const int32_t* __rest
   for (int it = 0; it < kPermChunk / 64; ++it) {
     const int64_t f = (int64_t)c * kPermChunk + it * 64 + lane;
     const bool valid = f < S;
-    const int e = valid ? idx[f] : -1;
-    uint64_t todo = __ballot(valid);
-    int r = 0;
-    while (todo) {
-      const int leader = __ffsll((unsigned long long)todo) - 1;
-      const int le = __shfl(e, leader, 64);
-      const uint64_t m = __ballot(e == le);
-      const int base = cnt[le];
-      if (e == le) r = base + __popcll(m & lt_mask);
-      __builtin_amdgcn_wave_barrier();
-      if (lane == leader) cnt[le] = base + __popcll(m);
-      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
-      __builtin_amdgcn_wave_barrier();
-      todo &= ~m;
+    const int e = valid ? idx[f] : 0;
+    // the lanes holding the same expert, from one ballot per bit of the id
+    uint64_t peers = __ballot(valid);
+#pragma unroll
+    for (int bit = 0; bit < kPermIdBits; ++bit) {
+      const bool set = (e >> bit) & 1;
+      const uint64_t m = __ballot(valid && set);
+      peers &= set ? m : ~m;
     }
-    if (valid) rank[f] = r;
+    const int before = __popcll(peers & lt_mask);  // equal experts in earlier slots
+    const int base = valid ? cnt[e] : 0;
+    __builtin_amdgcn_wave_barrier();
+    // the first lane of each expert advances its count
+    if (valid && before == 0) cnt[e] = base + __popcll(peers);
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+    __builtin_amdgcn_wave_barrier();
+    if (valid) rank[f] = base + before;
   }
   for (int i = lane; i < N; i += 64) hist[(int64_t)c * N + i] = cnt[i];
 }

@@ -7,29 +7,82 @@ namespace moe {
 
 __device__ __forceinline__ int lane_id() { return threadIdx.x & 63; }
 
-// Butterfly reductions: at every stage lanes i and i^m combine the same two
-// partials (commutatively), so every lane ends with the identical value.
-__device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+// Max over the wavefront in every lane, on the VALU (DPP and lane swaps, no
+// LDS round trips): partners lane^1 and lane^2 (quad permutes), then the
+// mirrored lane of each 8-lane half-row and of each 16-lane row (after the
+// earlier steps every group being paired holds one value, so a mirror pairs
+// groups as an xor would), then the neighbouring row and the other half of
+// the wavefront (v_permlane16_swap / v_permlane32_swap of a value with itself
+// hand every lane its own value and its partner's).  Max is exact, so every
+// lane ends with the identical value.
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp_u32(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, 0xf, 0xf, false);
+}
+constexpr int kDppXor1 = 0xb1;        // quad_perm [1, 0, 3, 2]
+constexpr int kDppXor2 = 0x4e;        // quad_perm [2, 3, 0, 1]
+constexpr int kDppRowMirror = 0x140;  // lane i <-> 15 - i within a row
+constexpr int kDppHalfMirror = 0x141; // lane i <-> 7 - i within a half-row
+
+template <class T, class Step>
+__device__ __forceinline__ T wave_reduce_exact(T v, Step&& step) {
+  v = step.template dpp<kDppXor1>(v);
+  v = step.template dpp<kDppXor2>(v);
+  v = step.template dpp<kDppHalfMirror>(v);
+  v = step.template dpp<kDppRowMirror>(v);
+  v = step.swap16(v);
+  v = step.swap32(v);
   return v;
 }
+
+struct MaxF32Step {
+  template <int C>
+  __device__ __forceinline__ float dpp(float v) const {
+    return fmaxf(v, __uint_as_float(dpp_u32<C>(__float_as_uint(v))));
+  }
+  __device__ __forceinline__ float swap16(float v) const {
+    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+  }
+  __device__ __forceinline__ float swap32(float v) const {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+  }
+};
+
+struct MaxU64Step {
+  static __device__ __forceinline__ uint64_t mx(uint64_t a, uint64_t b) { return a > b ? a : b; }
+  static __device__ __forceinline__ uint64_t pack(uint32_t hi, uint32_t lo) {
+    return ((uint64_t)hi << 32) | lo;
+  }
+  template <int C>
+  __device__ __forceinline__ uint64_t dpp(uint64_t v) const {
+    return mx(v, pack(dpp_u32<C>((uint32_t)(v >> 32)), dpp_u32<C>((uint32_t)v)));
+  }
+  __device__ __forceinline__ uint64_t swap16(uint64_t v) const {
+    const uint32_t lo = (uint32_t)v, hi = (uint32_t)(v >> 32);
+    const auto l = __builtin_amdgcn_permlane16_swap(lo, lo, false, false);
+    const auto h = __builtin_amdgcn_permlane16_swap(hi, hi, false, false);
+    return mx(pack(h[0], l[0]), pack(h[1], l[1]));
+  }
+  __device__ __forceinline__ uint64_t swap32(uint64_t v) const {
+    const uint32_t lo = (uint32_t)v, hi = (uint32_t)(v >> 32);
+    const auto l = __builtin_amdgcn_permlane32_swap(lo, lo, false, false);
+    const auto h = __builtin_amdgcn_permlane32_swap(hi, hi, false, false);
+    return mx(pack(h[0], l[0]), pack(h[1], l[1]));
+  }
+};
+
+__device__ __forceinline__ float wave_max(float v) { return wave_reduce_exact(v, MaxF32Step{}); }
+__device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
+  return wave_reduce_exact(v, MaxU64Step{});
+}
+
+// Butterfly sum: at every stage lanes i and i^m add the same two partials
+// (commutatively), so every lane ends with the identical value.
 __device__ __forceinline__ float wave_sum(float v) {
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, 64);
-  return v;
-}
-__device__ __forceinline__ uint64_t shfl_xor_u64(uint64_t v, int o) {
-  uint32_t lo = __shfl_xor((uint32_t)v, o, 64);
-  uint32_t hi = __shfl_xor((uint32_t)(v >> 32), o, 64);
-  return ((uint64_t)hi << 32) | lo;
-}
-__device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) {
-    uint64_t w = shfl_xor_u64(v, o);
-    v = w > v ? w : v;
-  }
   return v;
 }
 
