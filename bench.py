@@ -163,13 +163,17 @@ def run_workload(name, steps, warmup, events: HipEvents, extra=False, one_stream
     for _ in range(warmup):
         step(None)
     torch.cuda.synchronize()
-    arrays = [ev_arr_t(*evs[i * 2 * len(STAGES):(i + 1) * 2 * len(STAGES)]) for i in range(steps)]
-    torch.cuda.synchronize()
+    # the timed steps carry no stage events; the per-stage times come from as
+    # many steps again, each stage bracketed by events on its own stream
     t_start = time.perf_counter()
+    for i in range(steps):
+        step(None)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t_start
+    arrays = [ev_arr_t(*evs[i * 2 * len(STAGES):(i + 1) * 2 * len(STAGES)]) for i in range(steps)]
     for i in range(steps):
         step(arrays[i])
     torch.cuda.synchronize()
-    elapsed = time.perf_counter() - t_start
     stage_ms = {s: [] for s in STAGES}
     for i in range(steps):
         base = i * 2 * len(STAGES)
@@ -401,7 +405,7 @@ def main():
     }
     inp = r.pop("inputs")
     if not args.no_decode:
-        d = run_workload("v3_decode", args.steps, args.warmup, events)
+        d = run_workload("v3_decode", args.steps, args.warmup, events, one_stream=args.one_stream)
         d.pop("inputs")
         line["decode"] = decode_summary(d)
     if not args.no_cpu_baseline:

@@ -209,7 +209,7 @@ int moe_combine(const moe_config* cfg, const void* y_perm, const int32_t* slot_r
  * moe_forward - the whole layer: router -> permute -> routed experts (fused
  * gather) -> combine.  The shared MLP runs on `stream_side`, overlapping the
  * routed path.  stream_side may be NULL or equal stream_main: then, with bf16
- * weights and one shared expert (S = 1), the shared expert runs inside the
+ * or fp8 weights and one shared expert (S = 1), the shared expert runs inside the
  * routed grouped GEMMs as one more group whose rows are all T tokens (results
  * are bitwise the same either way), and otherwise after the routed path.
  *   x [T, d];  W_r [N, d];  b [N] nullable

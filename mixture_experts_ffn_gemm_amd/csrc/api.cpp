@@ -35,10 +35,12 @@ struct Layout {
   int64_t h_elems;  // capacity of the h region in activation elements
 };
 
-// bf16 with one shared expert and no second stream to overlap it on: the
-// shared expert runs inside the routed grouped GEMMs as one more group (its
-// rows: every token, in order).  The workspace is sized for both ways.
-bool can_fold_shared(const moe_config& c) { return c.w_dtype == MOE_BF16 && c.n_shared == 1; }
+// bf16 or fp8 with one shared expert and no second stream to overlap it on:
+// the shared expert runs inside the routed grouped GEMMs as one more group
+// (its rows: every token, in order).  The workspace is sized for both ways.
+bool can_fold_shared(const moe_config& c) {
+  return (c.w_dtype == MOE_BF16 || c.w_dtype == MOE_FP8_E4M3) && c.n_shared == 1;
+}
 
 Layout make_layout(const moe_config& c) {
   Layout L{};
@@ -190,10 +192,13 @@ int run_expert_ffn(const moe_config* c, int n_experts, const int32_t* offsets, i
                    const float* s2, void* h, void* y_rows, hipStream_t s,
                    void* const* ev = nullptr, int stage_up = -1, int stage_dn = -1,
                    const void* W1x = nullptr, const void* W3x = nullptr,
-                   const void* W2x = nullptr) {
+                   const void* W2x = nullptr, const float* s1x = nullptr,
+                   const float* s3x = nullptr, const float* s2x = nullptr) {
   GroupedGemmArgs up{};
   up.B0x = W1x;
   up.B1x = W3x;
+  up.S0x = s1x;
+  up.S1x = s3x;
   up.A = x_rows;
   up.row_index = row_index;
   up.offsets = offsets;
@@ -208,6 +213,7 @@ int run_expert_ffn(const moe_config* c, int n_experts, const int32_t* offsets, i
   up.K = c->d;
   GroupedGemmArgs dn{};
   dn.B0x = W2x;
+  dn.S0x = s2x;
   dn.A = h;
   dn.row_index = nullptr;
   dn.offsets = offsets;
@@ -465,7 +471,7 @@ static int forward_impl(const moe_config* cfg, const void* x, const float* W_r, 
     // routed experts and the shared expert (group n_routed) in one launch each
     st = run_expert_ffn(cfg, c.n_routed + 1, offsets, slots + c.T, c.inter, x, row_token, W1, W3,
                         W2, s1, s3, s2, at<void>(ws, L.h), y, sm, ev, MOE_STAGE_UP,
-                        MOE_STAGE_DOWN, W1s, W3s, W2s);
+                        MOE_STAGE_DOWN, W1s, W3s, W2s, s1s, s3s, s2s);
     ys = (char*)y + slots * c.d * act_bytes(c.act_dtype);
     for (int stg : {MOE_STAGE_SHARED_UP, MOE_STAGE_SHARED_DOWN}) {  // folded: empty intervals
       MOE_HIP_CHECK(mark(ev, stg, false, sm));

@@ -88,16 +88,18 @@ __device__ __forceinline__ void tile(const GroupedGemmArgs& args, const TileCoor
   {
     int n = ncol0 + col;
     if (n > Nout - 1) n = Nout - 1;
-    const int64_t boff = ((int64_t)tc.group * Nout + n) * K + kg * 16;
+    // the shared expert folded in as the last group has weights of its own
+    const bool xg = args.B0x && tc.group == args.n_groups - 1;
+    const int g = xg ? 0 : __builtin_amdgcn_readfirstlane(tc.group);
+    const int64_t boff = ((int64_t)g * Nout + n) * K + kg * 16;
     // the wave's 16 columns lie in one 128-column scale block: scalar loads
-    const int g = __builtin_amdgcn_readfirstlane(tc.group);
     const int nb = __builtin_amdgcn_readfirstlane((ncol0 < Nout ? ncol0 : Nout - 1) >> 7);
     const int64_t soff = ((int64_t)g * (Nout / 128) + nb) * KB;
-    bp[0] = (const uint8_t*)args.B0 + boff;
-    sp[0] = (cfloat*)(args.S0 + soff);
+    bp[0] = (const uint8_t*)(xg ? args.B0x : args.B0) + boff;
+    sp[0] = (cfloat*)((xg ? args.S0x : args.S0) + soff);
     if (SWIGLU) {
-      bp[NB - 1] = (const uint8_t*)args.B1 + boff;
-      sp[NB - 1] = (cfloat*)(args.S1 + soff);
+      bp[NB - 1] = (const uint8_t*)(xg ? args.B1x : args.B1) + boff;
+      sp[NB - 1] = (cfloat*)((xg ? args.S1x : args.S1) + soff);
     }
   }
   // Activation staging: in chunk c, wave wv fills LDS rows 4wv .. 4wv+3 of

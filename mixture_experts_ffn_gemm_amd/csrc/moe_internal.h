@@ -88,10 +88,12 @@ struct GroupedGemmArgs {
   int64_t max_rows;
   const void* B0;           // [G, Nout, K]  (W1 or W2)
   const void* B1;           // [G, Nout, K]  (W3) for the SwiGLU epilogue, else null
-  const void* B0x;          // bf16 only: if non-null, the weights [Nout, K] of the last
-  const void* B1x;          //   group (the shared expert folded in as one more group)
+  const void* B0x;          // if non-null, the weights [Nout, K] of the last group (the
+  const void* B1x;          //   shared expert folded in as one more group)
   const float* S0;          // fp8 block scales [G, Nout/128, K/128] or null
   const float* S1;
+  const float* S0x;         // fp8: the block scales [Nout/128, K/128] of B0x / B1x
+  const float* S1x;
   void* C;                  // [rows, Nout]
   int Nout;
   int K;

@@ -359,11 +359,11 @@ def test_forward_deterministic_and_bf16_out(lib):
     assert torch.equal(c16, a.to(torch.bfloat16))
 
 
-@pytest.mark.parametrize("name", ["deepseekmoe_2b", "v2_shaped", "v3_prefill"])
+@pytest.mark.parametrize("name", ["deepseekmoe_2b", "v2_shaped", "v3_prefill", "v3_decode"])
 def test_forward_one_stream(lib, name):
-    """Without a second stream the one shared expert of bf16 layers runs as one
-    more group of the routed grouped GEMMs (V3: 256 routed + 1 shared groups);
-    the result is bitwise that of the two-stream forward."""
+    """Without a second stream the one shared expert of bf16 and fp8 layers runs
+    as one more group of the routed grouped GEMMs (V3: 256 routed + 1 shared
+    groups); the result is bitwise that of the two-stream forward."""
     cfg = small_cfg(name)
     say(f"[forward-one-stream] {name} N={cfg.n_routed} S={cfg.n_shared}")
     inp = datagen.MoEInputs(cfg)
