@@ -233,6 +233,15 @@ int run_expert_ffn(const moe_config* c, int n_experts, const int32_t* offsets, i
       return launch_gemm_bf16_persist(a, swiglu, s);
     return launch_gemm_bf16_v2(a, swiglu, s);
   };
+  // fp8: many rows per expert (prefill) take the persistent MFMA kernel with
+  // the weights dequantized to bf16 in registers; a few rows per expert
+  // (decode) the weight-streaming kernel
+  auto fp8_gemm = [&](const GroupedGemmArgs& a, bool swiglu, int64_t a_rows) {
+    if (a.max_rows >= 128 * (int64_t)a.n_groups && a.K >= 128 &&
+        a_rows * (int64_t)a.K * 2 < (int64_t(1) << 32) - 4096)
+      return launch_gemm_fp8_persist(a, swiglu, s);
+    return swiglu ? launch_gemm_fp8_swiglu(a, s) : launch_gemm_fp8_store(a, s);
+  };
   const int64_t up_rows = row_index ? (c->T > max_rows ? c->T : max_rows) : max_rows;
   MOE_HIP_CHECK(mark(ev, stage_up, false, s));
   if (c->w_dtype == MOE_F32)
@@ -240,7 +249,7 @@ int run_expert_ffn(const moe_config* c, int n_experts, const int32_t* offsets, i
   else if (c->w_dtype == MOE_BF16)
     MOE_HIP_CHECK(bf16_gemm(up, true, up_rows));
   else
-    MOE_HIP_CHECK(launch_gemm_fp8_swiglu(up, s));
+    MOE_HIP_CHECK(fp8_gemm(up, true, up_rows));
   MOE_HIP_CHECK(mark(ev, stage_up, true, s));
   MOE_HIP_CHECK(mark(ev, stage_dn, false, s));
   if (c->w_dtype == MOE_F32)
@@ -248,7 +257,7 @@ int run_expert_ffn(const moe_config* c, int n_experts, const int32_t* offsets, i
   else if (c->w_dtype == MOE_BF16)
     MOE_HIP_CHECK(bf16_gemm(dn, false, max_rows));
   else
-    MOE_HIP_CHECK(launch_gemm_fp8_store(dn, s));
+    MOE_HIP_CHECK(fp8_gemm(dn, false, max_rows));
   MOE_HIP_CHECK(mark(ev, stage_dn, true, s));
   return MOE_OK;
 }

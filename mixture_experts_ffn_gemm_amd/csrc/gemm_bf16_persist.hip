@@ -43,6 +43,18 @@
 // fetched into LDS by a direct load too, so no load result is ever waited for
 // in registers.  LDS rows hold BK bf16 of one matrix row; their 16-byte chunks
 // are XOR-swizzled so the fragment reads are free of bank conflicts.
+//
+// fp8 weights (W8).  The weights may be OCP e4m3fn codes with one fp32 scale
+// per 128 x 128 block (open-model-atlas, "DeepSeek-V3.2-Exp - Mixture of
+// experts", the parameter table's note on FP8 block scales).  Their LDS rows
+// then hold 32 codes (two 16-byte halves, the halves of rows 8..15 of every
+// 16 swapped so 16 lanes' reads cover all banks); a lane reads its 16 codes for
+// both k-steps of a step at once and dequantizes them to bf16 as
+// bf16(code * scale) (code to fp32 exactly, one fp32 multiply, round to nearest
+// even) just before its MFMAs.  The k-values a lane group feeds to one MFMA
+// are then 16g + 8ks + 0..7 rather than 8(2ks + g) + 0..7; the activation
+// fragments follow the same assignment, so every MFMA still pairs equal k.
+// A step's tile is 16 KiB of activations and 8 KiB of codes.
 #include "grouped_sched.h"
 #include "moe_internal.h"
 
@@ -54,26 +66,38 @@ typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 typedef unsigned u32x4_t __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
 typedef __attribute__((address_space(3))) void lds_void;
+// block scales are wave-uniform: constant-address loads become scalar loads
+typedef __attribute__((address_space(4))) const float cfloat;
 
 constexpr int BM = 256, BN = 256, NTHR = 256, NWAVE = 4, MB = 4, NT = 4;
 
-template <int BK>
+template <int BK, bool W8>
 struct Geo {
-  static constexpr int ROW_BYTES = BK * 2;
-  static constexpr int CPR = BK / 8;                      // 16-byte chunks per LDS row
+  static_assert(!W8 || BK == 32, "fp8 rows are two 16-byte halves");
+  static constexpr int ROW_BYTES = BK * 2;                // activation LDS row
+  static constexpr int B_ROW_BYTES = W8 ? BK : BK * 2;    // weight LDS row
+  static constexpr int CPR = BK / 8;                      // 16-byte chunks per activation row
   static constexpr int A_BYTES = BM * ROW_BYTES;
-  static constexpr int STAGE_BYTES = (BM + BN) * ROW_BYTES;
+  static constexpr int B_BYTES = BN * B_ROW_BYTES;
+  static constexpr int STAGE_BYTES = A_BYTES + B_BYTES;
   static constexpr int LOADS = STAGE_BYTES / (NTHR * 16); // direct loads per thread per step
   static constexpr int A_LOADS = A_BYTES / (NTHR * 16);
   static constexpr int ROWS_PER_KB = 1024 / ROW_BYTES;
+  static constexpr int B_ROWS_PER_KB = 1024 / B_ROW_BYTES;
   static constexpr int ROWS_PER_256 = 256 / ROW_BYTES;
   static constexpr int KS = BK / 16;                      // k-steps per step
+  static constexpr int B_STEP = BK * (W8 ? 1 : 2);        // weight bytes per row per step
   // A ds_read_b128 is served 16 lanes (256 B, all 64 banks) at a time; the
   // 16 consecutive rows a lane group reads then land on 16 distinct slots.
   static __device__ __forceinline__ int swz(int row, int chunk) {
     return chunk ^ ((row / ROWS_PER_256) & (CPR - 1));
   }
+  // fp8 weight rows: 16-byte half h of row r sits at position h ^ ((r >> 3) & 1)
+  static __device__ __forceinline__ int swz8(int row, int half) { return half ^ ((row >> 3) & 1); }
+  // activation chunk of lane group g (lane >> 5) in k-step ks
+  static __device__ __forceinline__ int achunk(int ks, int g) { return W8 ? 2 * g + ks : 2 * ks + g; }
 };
 
 // LDS row of column tile j of wave column wn.  Up: tiles 0, 1 are W1 rows,
@@ -96,21 +120,73 @@ struct Frags {
   bf16x8_t a[MB], b[NT];
 };
 
-template <int BK, bool SWIGLU>
-__device__ __forceinline__ void read_frags(const char* stage, int ks, int wm, int wn, int lane,
-                                           Frags& f) {
-  using G = Geo<BK>;
-  const int l32 = lane & 31, chunk = 2 * ks + (lane >> 5);
-#pragma unroll
-  for (int j = 0; j < NT; ++j) {
-    const int r = brow<SWIGLU>(wn, j) + l32;
-    f.b[j] = *(const bf16x8_t*)(stage + G::A_BYTES + r * G::ROW_BYTES + (G::swz(r, chunk) << 4));
-  }
+template <int BK, bool SWIGLU, bool W8>
+__device__ __forceinline__ void read_a(const char* stage, int ks, int wm, int lane, Frags& f) {
+  using G = Geo<BK, W8>;
+  const int l32 = lane & 31, chunk = G::achunk(ks, lane >> 5);
 #pragma unroll
   for (int i = 0; i < MB; ++i) {
     const int r = (2 * i + wm) * 32 + l32;
     f.a[i] = *(const bf16x8_t*)(stage + r * G::ROW_BYTES + (G::swz(r, chunk) << 4));
   }
+}
+
+template <int BK, bool SWIGLU>
+__device__ __forceinline__ void read_frags(const char* stage, int ks, int wm, int wn, int lane,
+                                           Frags& f) {
+  using G = Geo<BK, false>;
+  const int l32 = lane & 31, chunk = G::achunk(ks, lane >> 5);
+#pragma unroll
+  for (int j = 0; j < NT; ++j) {
+    const int r = brow<SWIGLU>(wn, j) + l32;
+    f.b[j] = *(const bf16x8_t*)(stage + G::A_BYTES + r * G::ROW_BYTES + (G::swz(r, chunk) << 4));
+  }
+  read_a<BK, SWIGLU, false>(stage, ks, wm, lane, f);
+}
+
+// fp8 weights: the two block scales of this wave's columns in one step (W1
+// and W3 for the up projection; the down projection uses s0 for all).
+struct StepScale {
+  float s0, s1;
+};
+
+// 8 e4m3 codes -> bf16(code * s), round to nearest even
+__device__ __forceinline__ bf16x8_t dequant8(uint32_t w0, uint32_t w1, float s) {
+  const f32x2_t a = __builtin_amdgcn_cvt_pk_f32_fp8(w0, false);
+  const f32x2_t b = __builtin_amdgcn_cvt_pk_f32_fp8(w0, true);
+  const f32x2_t c = __builtin_amdgcn_cvt_pk_f32_fp8(w1, false);
+  const f32x2_t d = __builtin_amdgcn_cvt_pk_f32_fp8(w1, true);
+  return bf16x8_t{(__bf16)(a[0] * s), (__bf16)(a[1] * s), (__bf16)(b[0] * s), (__bf16)(b[1] * s),
+                  (__bf16)(c[0] * s), (__bf16)(c[1] * s), (__bf16)(d[0] * s), (__bf16)(d[1] * s)};
+}
+
+// First k-step of a step with fp8 weights: the lane's 16 codes of each column
+// tile for both k-steps (kept in `raw`), the first 8 dequantized.
+template <int BK, bool SWIGLU>
+__device__ __forceinline__ void read_frags_w8_first(const char* stage, int wm, int wn, int lane,
+                                                    StepScale sc, u32x4_t (&raw)[NT], Frags& f) {
+  using G = Geo<BK, true>;
+  const int l32 = lane & 31, g = lane >> 5;
+#pragma unroll
+  for (int j = 0; j < NT; ++j) {
+    const int r = brow<SWIGLU>(wn, j) + l32;
+    raw[j] = *(const u32x4_t*)(stage + G::A_BYTES + r * G::B_ROW_BYTES + (G::swz8(r, g) << 4));
+  }
+  read_a<BK, SWIGLU, true>(stage, 0, wm, lane, f);
+#pragma unroll
+  for (int j = 0; j < NT; ++j)
+    f.b[j] = dequant8(raw[j][0], raw[j][1], SWIGLU && j >= 2 ? sc.s1 : sc.s0);
+}
+
+// Second k-step: the other 8 codes of `raw`.
+template <int BK, bool SWIGLU>
+__device__ __forceinline__ void read_frags_w8_second(const char* stage, int wm, int lane,
+                                                     StepScale sc, const u32x4_t (&raw)[NT],
+                                                     Frags& f) {
+  read_a<BK, SWIGLU, true>(stage, 1, wm, lane, f);
+#pragma unroll
+  for (int j = 0; j < NT; ++j)
+    f.b[j] = dequant8(raw[j][2], raw[j][3], SWIGLU && j >= 2 ? sc.s1 : sc.s0);
 }
 
 // The four MFMAs of row block i of one k-step.
@@ -155,9 +231,9 @@ __device__ __forceinline__ Tile decode_tile(const TileTab& tt, int n_groups, int
 // The issue side of the pipeline: which step's slice the next direct loads
 // fetch, and their sources in the current tile: a wave-uniform base per load
 // and a 32-bit per-lane byte offset.
-template <int BK, bool SWIGLU>
+template <int BK, bool SWIGLU, bool W8>
 struct Issuer {
-  using G = Geo<BK>;
+  using G = Geo<BK, W8>;
   const char* base[G::LOADS];
   unsigned off[G::LOADS];
   int it, kt;  // tile index within this workgroup's list, step within the tile
@@ -165,7 +241,8 @@ struct Issuer {
   __device__ __forceinline__ void build(const GroupedGemmArgs& a, const TileTab& tt,
                                         const Tile& t, int wv, int lane) {
     const int rib = lane / G::CPR, phys = lane % G::CPR;
-    const int64_t rowb = (int64_t)a.K * 2;  // bytes per matrix row
+    const int64_t rowb = (int64_t)a.K * 2;           // bytes per activation row
+    const int64_t browb = (int64_t)a.K * (W8 ? 1 : 2);  // bytes per weight row
 #pragma unroll
     for (int j = 0; j < G::LOADS; ++j) {
       const int blk = NWAVE * j + wv;
@@ -181,7 +258,11 @@ struct Issuer {
         base[j] = (const char*)a.A;
         off[j] = (unsigned)(row * rowb) + (unsigned)(G::swz(r, phys) << 4);
       } else {
-        const int r0 = (blk - G::A_BYTES / 1024) * G::ROWS_PER_KB;  // first LDS row, 0..255
+        // first LDS row of the block (0..255), this lane's row in it, and the
+        // 16-byte piece of the row's step slice that goes to this lane's slot
+        const int r0 = (blk - G::A_BYTES / 1024) * G::B_ROWS_PER_KB;
+        const int rl = W8 ? lane >> 1 : rib;
+        const int piece = W8 ? G::swz8(r0 + rl, lane & 1) : G::swz(r0 + rl, phys);
         const bool w3 = SWIGLU && r0 >= 128;
         int n = t.n0 + (SWIGLU ? (r0 & 127) : r0);
         int lim = a.Nout - 1 - n;  // rows past the last weight row repeat it
@@ -190,21 +271,45 @@ struct Issuer {
           lim = 0;
         }
         if (a.B0x && t.g == a.n_groups - 1)  // the folded shared expert
-          base[j] = (const char*)(w3 ? a.B1x : a.B0x) + (int64_t)n * rowb;
+          base[j] = (const char*)(w3 ? a.B1x : a.B0x) + (int64_t)n * browb;
         else
-          base[j] = (const char*)(w3 ? a.B1 : a.B0) + ((int64_t)t.g * a.Nout + n) * rowb;
-        off[j] = (unsigned)((rib < lim ? rib : lim) * rowb) +
-                 (unsigned)(G::swz(r0 + rib, phys) << 4);
+          base[j] = (const char*)(w3 ? a.B1 : a.B0) + ((int64_t)t.g * a.Nout + n) * browb;
+        off[j] = (unsigned)((rl < lim ? rl : lim) * browb) + (unsigned)(piece << 4);
       }
     }
   }
 
   // Direct load j of the current step into `stage`.
   __device__ __forceinline__ void load(int j, char* stage, int wv) const {
-    __builtin_amdgcn_global_load_lds((const void*)(base[j] + kt * (BK * 2) + off[j]),
+    const int step = j < G::A_LOADS ? BK * 2 : G::B_STEP;
+    __builtin_amdgcn_global_load_lds((const void*)(base[j] + kt * step + off[j]),
                                      (lds_void*)(stage + (NWAVE * j + wv) * 1024), 16, 0, 0);
   }
 };
+
+// fp8 weights: where this wave's block scales of a tile start (one 128-row
+// block of W1 and of W3 for the up projection, of W2 for the down projection).
+struct TileScale {
+  cfloat *p0, *p1;
+};
+template <bool SWIGLU>
+__device__ __forceinline__ TileScale tile_scale(const GroupedGemmArgs& a, const Tile& t, int wn) {
+  const int KB = a.K / 128, NBL = a.Nout / 128;
+  int nb = (t.n0 >> 7) + (SWIGLU ? 0 : wn);
+  if (nb > NBL - 1) nb = NBL - 1;  // columns past Nout: computed, never stored
+  nb = __builtin_amdgcn_readfirstlane(nb);
+  const int g = __builtin_amdgcn_readfirstlane(t.g);
+  const bool xg = a.B0x && g == a.n_groups - 1;
+  const int64_t o = ((xg ? 0 : (int64_t)g * NBL) + nb) * KB;
+  TileScale ts;
+  ts.p0 = (cfloat*)((xg ? a.S0x : a.S0) + o);
+  ts.p1 = SWIGLU ? (cfloat*)((xg ? a.S1x : a.S1) + o) : ts.p0;
+  return ts;
+}
+// the scales of step kt (32 values of K; 4 steps per 128-wide block)
+__device__ __forceinline__ StepScale step_scale(const TileScale& ts, int kt) {
+  return StepScale{ts.p0[kt >> 2], ts.p1[kt >> 2]};
+}
 
 // The gathered row indices of tile `t` into ri[b]: wave wv fetches 64 of them.
 __device__ __forceinline__ void fetch_rows(const GroupedGemmArgs& a, TileTab& tt, int b,
@@ -224,8 +329,8 @@ struct Sched {
 // tile, rebuilds the sources (from row indices fetched a tile earlier) and
 // fetches the row indices of the tile after it.  Past the last tile the last
 // step is loaded again, into stages that are never read.
-template <int BK, bool SWIGLU>
-__device__ __forceinline__ void advance(Issuer<BK, SWIGLU>& is, const GroupedGemmArgs& a,
+template <int BK, bool SWIGLU, bool W8>
+__device__ __forceinline__ void advance(Issuer<BK, SWIGLU, W8>& is, const GroupedGemmArgs& a,
                                         TileTab& tt, const Sched& sc, int nk, int wv, int lane) {
   if (++is.kt < nk) return;
   if (is.it + 1 >= sc.ntile) {
@@ -310,13 +415,17 @@ __device__ __forceinline__ void store_tile(const GroupedGemmArgs& a, const Tile&
 // the sequence reads stage g % NS; during it the loads of step g+NS-1 go into
 // stage (g-1) % NS, which every wave finished reading before barrier B(g).
 // B(g+1) follows this thread's wait for its loads of step g+1 and for all its
-// LDS reads: after it step g+1 has landed for every thread.
-template <int BK, int NS, bool SWIGLU>
-__device__ __forceinline__ void run_tile(int& g, int nk, Issuer<BK, SWIGLU>& is,
+// LDS reads: after it step g+1 has landed for every thread.  fp8 weights: `ss`
+// holds the block scales of the current step on entry and of the next one
+// (the next tile's first, `tsn`, after the last step) on return.
+template <int BK, int NS, bool SWIGLU, bool W8>
+__device__ __forceinline__ void run_tile(int& g, int nk, Issuer<BK, SWIGLU, W8>& is,
                                          const GroupedGemmArgs& a, TileTab& tt, const Sched& sc,
-                                         char (*st)[Geo<BK>::STAGE_BYTES], int wm, int wn, int wv,
-                                         int lane, Frags (&f)[2], f32x16_t (&acc)[MB][NT]) {
-  using G = Geo<BK>;
+                                         char (*st)[Geo<BK, W8>::STAGE_BYTES], int wm, int wn,
+                                         int wv, int lane, Frags (&f)[2], f32x16_t (&acc)[MB][NT],
+                                         const TileScale& tsc, const TileScale& tsn, StepScale& ss,
+                                         u32x4_t (&raw)[NT]) {
+  using G = Geo<BK, W8>;
   constexpr int KS = G::KS, LOADS = G::LOADS;
   // row groups of four MFMAs before the barrier of a step, and the loads
   // issued after each
@@ -324,6 +433,14 @@ __device__ __forceinline__ void run_tile(int& g, int nk, Issuer<BK, SWIGLU>& is,
   for (int kt = 0; kt < nk; ++kt, ++g) {
     const char* cur = st[g % NS];
     char* dst = st[(g + NS - 1) % NS];
+    StepScale ss_next{0.f, 0.f};
+    if (W8) {
+      // scalar loads, early: the scales of the step whose fragments the
+      // barrier of this step reads
+      const bool last = kt + 1 >= nk;
+      const TileScale& tn = last ? tsn : tsc;
+      ss_next = step_scale(tn, last ? 0 : kt + 1);
+    }
 #pragma unroll
     for (int s = 0; s < KS; ++s) {
       const Frags& fc = f[s & 1];
@@ -335,7 +452,10 @@ __device__ __forceinline__ void run_tile(int& g, int nk, Issuer<BK, SWIGLU>& is,
           // B(g+1), then the fragments of the next step's first k-step
           wait_vm_lgkm<(NS - 2) * LOADS>();
           __builtin_amdgcn_s_barrier();
-          read_frags<BK, SWIGLU>(st[(g + 1) % NS], 0, wm, wn, lane, fn);
+          if (W8)
+            read_frags_w8_first<BK, SWIGLU>(st[(g + 1) % NS], wm, wn, lane, ss_next, raw, fn);
+          else
+            read_frags<BK, SWIGLU>(st[(g + 1) % NS], 0, wm, wn, lane, fn);
           __builtin_amdgcn_sched_barrier(0);
         }
         mfma_row(i, fc, acc);
@@ -346,18 +466,24 @@ __device__ __forceinline__ void run_tile(int& g, int nk, Issuer<BK, SWIGLU>& is,
 #pragma unroll
           for (int j = 0; j < LOADS; ++j)
             if (j >= (LOADS * grp) / GROUPS && j < upto) is.load(j, dst, wv);
-          if (grp == GROUPS - 1) advance<BK, SWIGLU>(is, a, tt, sc, nk, wv, lane);
+          if (grp == GROUPS - 1) advance<BK, SWIGLU, W8>(is, a, tt, sc, nk, wv, lane);
         }
-        if (i == 0 && s < KS - 1) read_frags<BK, SWIGLU>(cur, s + 1, wm, wn, lane, fn);
+        if (i == 0 && s < KS - 1) {
+          if (W8)
+            read_frags_w8_second<BK, SWIGLU>(cur, wm, lane, ss, raw, fn);
+          else
+            read_frags<BK, SWIGLU>(cur, s + 1, wm, wn, lane, fn);
+        }
         __builtin_amdgcn_sched_barrier(0);
       }
     }
+    if (W8) ss = ss_next;
   }
 }
 
-template <int BK, int NS, bool SWIGLU>
+template <int BK, int NS, bool SWIGLU, bool W8>
 __global__ __launch_bounds__(NTHR, 1) void gemm_bf16_persist_kernel(GroupedGemmArgs args) {
-  using G = Geo<BK>;
+  using G = Geo<BK, W8>;
   // one LDS object: the stages, then the tile table
   __shared__ __attribute__((aligned(1024))) char smem[NS * G::STAGE_BYTES + sizeof(TileTab)];
   char(*st)[G::STAGE_BYTES] = (char(*)[G::STAGE_BYTES])smem;
@@ -394,7 +520,7 @@ __global__ __launch_bounds__(NTHR, 1) void gemm_bf16_persist_kernel(GroupedGemmA
     wait_vm_lgkm<0>();
     __syncthreads();
   }
-  Issuer<BK, SWIGLU> is;
+  Issuer<BK, SWIGLU, W8> is;
   is.it = 0;
   is.kt = 0;
   is.build(args, tt, t, wv, lane);
@@ -405,7 +531,7 @@ __global__ __launch_bounds__(NTHR, 1) void gemm_bf16_persist_kernel(GroupedGemmA
   for (int s = 0; s < NS - 1; ++s) {
 #pragma unroll
     for (int j = 0; j < G::LOADS; ++j) is.load(j, st[s], wv);
-    advance<BK, SWIGLU>(is, args, tt, sc, nk, wv, lane);
+    advance<BK, SWIGLU, W8>(is, args, tt, sc, nk, wv, lane);
   }
   // The row indices of the tile after the next are fetched when the issuer
   // enters a tile and read when it enters the next one, at least NS-1 steps
@@ -414,25 +540,42 @@ __global__ __launch_bounds__(NTHR, 1) void gemm_bf16_persist_kernel(GroupedGemmA
   __builtin_amdgcn_s_barrier();  // B(0)
 
   Frags f[2];
-  read_frags<BK, SWIGLU>(st[0], 0, wm, wn, lane, f[0]);
+  u32x4_t raw[NT];
+  TileScale tsc{}, tsn{};
+  StepScale ss{0.f, 0.f};
+  if (W8) {
+    tsc = tile_scale<SWIGLU>(args, t, wn);
+    ss = step_scale(tsc, 0);
+    read_frags_w8_first<BK, SWIGLU>(st[0], wm, wn, lane, ss, raw, f[0]);
+  } else {
+    read_frags<BK, SWIGLU>(st[0], 0, wm, wn, lane, f[0]);
+  }
   f32x16_t acc[MB][NT];
   int g = 0;
   for (int i = 0; i < sc.ntile; ++i) {
-    if (i > 0) t = decode_tile(tt, sc.n_groups, sc.ntn, CN, sc.tile_id(i));
+    if (i > 0) {
+      t = decode_tile(tt, sc.n_groups, sc.ntn, CN, sc.tile_id(i));
+      if (W8) tsc = tsn;
+    }
+    if (W8)
+      tsn = i + 1 < sc.ntile
+                ? tile_scale<SWIGLU>(args, decode_tile(tt, sc.n_groups, sc.ntn, CN, sc.tile_id(i + 1)), wn)
+                : tsc;
 #pragma unroll
     for (int r = 0; r < MB; ++r)
 #pragma unroll
       for (int c = 0; c < NT; ++c)
 #pragma unroll
         for (int e = 0; e < 16; ++e) acc[r][c][e] = 0.f;
-    run_tile<BK, NS, SWIGLU>(g, nk, is, args, tt, sc, st, wm, wn, wv, lane, f, acc);
+    run_tile<BK, NS, SWIGLU, W8>(g, nk, is, args, tt, sc, st, wm, wn, wv, lane, f, acc, tsc, tsn,
+                                 ss, raw);
     store_tile<SWIGLU>(args, t, wm, wn, lane, acc);
   }
   // no load may still be writing LDS when the workgroup ends
   wait_vm_lgkm<0>();
 }
 
-constexpr int LIB_BK = 32, LIB_NS = 4;
+constexpr int LIB_BK = 32, LIB_NS = 4, LIB_NS_W8 = 4;
 
 }  // namespace gp
 
@@ -452,9 +595,19 @@ hipError_t launch_gemm_bf16_persist(const GroupedGemmArgs& a, bool swiglu, hipSt
   if (a.max_rows <= 0 || a.n_groups <= 0) return hipSuccess;
   const int grid = persist_grid();
   if (swiglu)
-    gp::gemm_bf16_persist_kernel<gp::LIB_BK, gp::LIB_NS, true><<<grid, gp::NTHR, 0, s>>>(a);
+    gp::gemm_bf16_persist_kernel<gp::LIB_BK, gp::LIB_NS, true, false><<<grid, gp::NTHR, 0, s>>>(a);
   else
-    gp::gemm_bf16_persist_kernel<gp::LIB_BK, gp::LIB_NS, false><<<grid, gp::NTHR, 0, s>>>(a);
+    gp::gemm_bf16_persist_kernel<gp::LIB_BK, gp::LIB_NS, false, false><<<grid, gp::NTHR, 0, s>>>(a);
+  return hipGetLastError();
+}
+
+hipError_t launch_gemm_fp8_persist(const GroupedGemmArgs& a, bool swiglu, hipStream_t s) {
+  if (a.max_rows <= 0 || a.n_groups <= 0) return hipSuccess;
+  const int grid = persist_grid();
+  if (swiglu)
+    gp::gemm_bf16_persist_kernel<gp::LIB_BK, gp::LIB_NS_W8, true, true><<<grid, gp::NTHR, 0, s>>>(a);
+  else
+    gp::gemm_bf16_persist_kernel<gp::LIB_BK, gp::LIB_NS_W8, false, true><<<grid, gp::NTHR, 0, s>>>(a);
   return hipGetLastError();
 }
 

@@ -102,6 +102,9 @@ struct GroupedGemmArgs {
 hipError_t launch_gemm_bf16_v2(const GroupedGemmArgs& a, bool swiglu, hipStream_t s);
 // persistent: one workgroup per CU, one pipeline across all of its tiles (K >= 128)
 hipError_t launch_gemm_bf16_persist(const GroupedGemmArgs& a, bool swiglu, hipStream_t s);
+// the same with fp8 block-scaled weights, dequantized to bf16 in registers
+// (K and Nout multiples of 128, K >= 128)
+hipError_t launch_gemm_fp8_persist(const GroupedGemmArgs& a, bool swiglu, hipStream_t s);
 int persist_grid();
 // fp32 SIMT (act f32, w f32)
 hipError_t launch_gemm_f32_swiglu(const GroupedGemmArgs& a, hipStream_t s);

@@ -187,23 +187,30 @@ def _rows_and_offsets(counts):
     return off, int(off[-1])
 
 
-@pytest.mark.parametrize("wdt", ["f32", "bf16", "fp8", "fp8_k384", "bf16_small_k", "bf16_many_tiles"])
+@pytest.mark.parametrize("wdt", ["f32", "bf16", "fp8", "fp8_k384", "fp8_prefill", "bf16_small_k",
+                                 "bf16_many_tiles"])
 def test_expert_ffn_ragged_groups(lib, wdt):
     """Groups of 0, 1, tile-1, tile, tile+1 and several tiles of rows.
 
     fp8 (d = 512, I = 384) and fp8_k384 (d = 384, I = 512): K / 128 of 4 and 3
     for the up projection, 3 and 4 for the down projection, so each projection
-    runs both its deep weight ring and its one-deep fallback.
+    runs both its deep weight ring and its one-deep fallback (fewer than 128
+    rows per expert on average: the weight-streaming kernel).  fp8_prefill:
+    more rows per expert, the persistent MFMA kernel, whose weights are
+    dequantized to bf16(code * scale); its bound models that rounding.
     bf16_small_k: K = 128 for both projections, the smallest K the bf16 path
     takes (four 32-deep steps per tile, as many as the pipeline has stages).
     bf16_many_tiles: more tiles than workgroups, so every persistent workgroup
     runs its pipeline across several tiles of different experts and fills."""
     d, I = {"f32": (256, 512), "bf16_small_k": (128, 128), "fp8_k384": (384, 512)}.get(wdt, (512, 384))
     counts = [0, 1, 127, 128, 129, 300, 0, 5, 64, 65]
+    if wdt == "fp8_prefill":
+        counts = [0, 1, 255, 256, 257, 600, 0, 130, 129, 300]
     if wdt == "bf16_many_tiles":
         counts = [int(c) for c in np.random.default_rng(11).integers(0, 700, 72)]
         counts[:6] = [0, 1, 255, 256, 257, 699]
-    name = {"f32": "gshard_fp32", "fp8": "v3_decode", "fp8_k384": "v3_decode"}.get(wdt, "deepseekmoe_2b")
+    name = {"f32": "gshard_fp32", "fp8": "v3_decode", "fp8_k384": "v3_decode",
+            "fp8_prefill": "v3_decode"}.get(wdt, "deepseekmoe_2b")
     cfg = datagen.get_config(name, d=d, inter=I, n_routed=len(counts), k=1, n_groups=1,
                              topk_groups=1, T=sum(counts), n_shared=0)
     say(f"[expert_ffn] {wdt} d={d} I={I} counts={counts}")
@@ -231,9 +238,11 @@ def test_expert_ffn_ragged_groups(lib, wdt):
         xs = x64[off[e]:off[e + 1]]
         ref[off[e]:off[e + 1]] = oracle.swiglu(xs, *w)
         if cfg.act_dtype == "bf16":
-            # the same contraction with h stored as bf16, as the kernels store it
-            g, u = xs @ w[0].T, xs @ w[1].T
-            ideal[off[e]:off[e + 1]] = round_bf16(g * oracle.sigmoid(g) * u) @ w[2].T
+            # the same contraction with h stored as bf16, as the kernels store
+            # it (and the dequantized weights rounded to bf16 where they are)
+            wk = tuple(round_bf16(wi) for wi in w) if wdt == "fp8_prefill" else w
+            g, u = xs @ wk[0].T, xs @ wk[1].T
+            ideal[off[e]:off[e + 1]] = round_bf16(g * oracle.sigmoid(g) * u) @ wk[2].T
     err = rel_err(got, ref)
     if cfg.act_dtype != "bf16":
         say(f"   rel err {err:.3e}")
@@ -343,6 +352,20 @@ def test_forward_full_size(lib, name):
     cfg = datagen.get_config(name)
     say(f"[forward-full] {name} T={cfg.T}")
     _forward_parity(lib, cfg)
+
+
+def test_forward_fp8_prefill(lib):
+    """fp8 block-scaled weights with many rows per expert (32 experts, 150 rows
+    each on average, and the 600-row shared expert) run the persistent MFMA
+    kernel; one-stream (shared expert folded in) and two-stream forwards agree
+    bitwise."""
+    cfg = datagen.get_config("v3_prefill", T=600, d=1024, inter=256, n_routed=32,
+                             w_dtype="fp8", w_block=datagen.FP8_BLOCK)
+    say(f"[forward-fp8-prefill] T={cfg.T} d={cfg.d} I={cfg.inter} N={cfg.n_routed}")
+    a = _forward_parity(lib, cfg)
+    dev = upload(datagen.MoEInputs(cfg))
+    b = _run_forward(lib, cfg, dev, side=False)[0]
+    assert torch.equal(a, b)
 
 
 def test_forward_deterministic_and_bf16_out(lib):
