@@ -126,13 +126,14 @@ def time_next_rows(moe, c, dev, counts, events: HipEvents, stream, reps=20):
     return out
 
 
-def run_workload(name, steps, warmup, events: HipEvents, extra=False, one_stream=False):
+def run_workload(name, steps, warmup, events: HipEvents, extra=False, one_stream=False,
+                 overrides=None):
     import torch
     import datagen
     from datagen.device import upload
     import mixture_experts_ffn_gemm_amd as moe
 
-    cfg = datagen.get_config(name)
+    cfg = datagen.get_config(name, **(overrides or {}))
     t0 = time.time()
     inp = datagen.MoEInputs(cfg)
     dev = upload(inp)
@@ -193,12 +194,32 @@ def run_workload(name, steps, warmup, events: HipEvents, extra=False, one_stream
     return res
 
 
+# the V3-shaped prefill with the decode workload's fp8 e4m3 weights and
+# 128 x 128 block scales
+FP8_PREFILL = dict(w_dtype="fp8", w_block=128)
+
+
+def fp8_prefill_summary(r):
+    """Whole-forward rate and the routed up GEMM's MFMA rate (bf16 MFMAs on the
+    dequantized weights) for the fp8-weight prefill."""
+    cfg = r.pop("cfg")
+    r.pop("inputs", None)
+    flops = 2.0 * cfg.T * cfg.k * cfg.d * 2 * cfg.inter
+    up_ms = r["stage_ms"]["up"]
+    return {"workload": "v3_prefill with fp8 e4m3 weights + 128x128 block scales",
+            "ms_per_step": round(r["ms_per_step"], 4),
+            "tokens_per_s": round(cfg.T / (r["ms_per_step"] * 1e-3), 1),
+            "up_ms": round(up_ms, 4), "down_ms": round(r["stage_ms"]["down"], 4),
+            "up_tflops": round(flops / (up_ms * 1e-3) / 1e12, 1),
+            "up_frac_bf16_peak": round(flops / (up_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)}
+
+
 def prefill_roofline(r):
     cfg = r["cfg"]
     flops = 2.0 * cfg.T * cfg.k * cfg.d * 2 * cfg.inter  # W1 and W3 over all T*k routed rows
     ms = r["stage_ms"]["up"]
     achieved = flops / (ms * 1e-3) / 1e12
-    return {"bound": "mfma", "kernel": "gp::gemm_bf16_persist_kernel<32, 4, true> (routed W1|W3 + SwiGLU)",
+    return {"bound": "mfma", "kernel": "gp::gemm_bf16_persist_kernel<32, 4, true, false> (routed W1|W3 + SwiGLU)",
             "achieved": round(achieved, 1), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
             "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
             "algorithmic_per_launch": flops, "avg_launch_ms": round(ms, 4),
@@ -332,7 +353,7 @@ def summarize_pmc(fetch_csv, write_csv, command):
     db = {"calibration": {"copy_bytes": COPY_CAL_BYTES, "fetch_counter_bytes": fetch[cal_f],
                           "write_counter_bytes": write[cal_w], "fetch_scale": sf, "write_scale": sw}}
     targets = {
-        "prefill_up": (lambda n: "gemm_bf16_persist_kernel<32, 4, true>" in n,
+        "prefill_up": (lambda n: "gemm_bf16_persist_kernel<32, 4, true, false>" in n,
                        ["gemm_bf16_persist.hip", "grouped_sched.h"]),
         "decode_up": (lambda n: "gemm_fp8_small_kernel<true" in n, ["gemm_fp8.hip", "grouped_sched.h"]),
     }
@@ -369,6 +390,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="v3_prefill")
     ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--no-fp8-prefill", action="store_true",
+                    help="skip the V3-shaped prefill with fp8 block-scaled weights")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--one-stream", action="store_true",
                     help="no side stream: the shared expert runs inside the routed GEMMs (bf16, S=1)")
@@ -404,6 +427,10 @@ def main():
         "next_rows": r.get("next_rows"),
     }
     inp = r.pop("inputs")
+    if not args.no_fp8_prefill:
+        line["next_rows"]["fp8_prefill"] = fp8_prefill_summary(
+            run_workload("v3_prefill", max(2, args.steps // 2), args.warmup, events,
+                         one_stream=args.one_stream, overrides=FP8_PREFILL))
     if not args.no_decode:
         d = run_workload("v3_decode", args.steps, args.warmup, events, one_stream=args.one_stream)
         d.pop("inputs")
