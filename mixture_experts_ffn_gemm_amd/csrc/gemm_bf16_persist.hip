@@ -160,11 +160,10 @@ __device__ __forceinline__ bf16x8_t dequant8(uint32_t w0, uint32_t w1, float s) 
                   (__bf16)(c[0] * s), (__bf16)(c[1] * s), (__bf16)(d[0] * s), (__bf16)(d[1] * s)};
 }
 
-// First k-step of a step with fp8 weights: the lane's 16 codes of each column
-// tile for both k-steps (kept in `raw`), the first 8 dequantized.
+// fp8 weights: the lane's 16 codes of each column tile for both k-steps of a
+// step (the first 8 for k-step 0, the last 8 for k-step 1).
 template <int BK, bool SWIGLU>
-__device__ __forceinline__ void read_frags_w8_first(const char* stage, int wm, int wn, int lane,
-                                                    StepScale sc, u32x4_t (&raw)[NT], Frags& f) {
+__device__ __forceinline__ void read_w8_raw(const char* stage, int wn, int lane, u32x4_t (&raw)[NT]) {
   using G = Geo<BK, true>;
   const int l32 = lane & 31, g = lane >> 5;
 #pragma unroll
@@ -172,21 +171,12 @@ __device__ __forceinline__ void read_frags_w8_first(const char* stage, int wm, i
     const int r = brow<SWIGLU>(wn, j) + l32;
     raw[j] = *(const u32x4_t*)(stage + G::A_BYTES + r * G::B_ROW_BYTES + (G::swz8(r, g) << 4));
   }
-  read_a<BK, SWIGLU, true>(stage, 0, wm, lane, f);
-#pragma unroll
-  for (int j = 0; j < NT; ++j)
-    f.b[j] = dequant8(raw[j][0], raw[j][1], SWIGLU && j >= 2 ? sc.s1 : sc.s0);
 }
-
-// Second k-step: the other 8 codes of `raw`.
-template <int BK, bool SWIGLU>
-__device__ __forceinline__ void read_frags_w8_second(const char* stage, int wm, int lane,
-                                                     StepScale sc, const u32x4_t (&raw)[NT],
-                                                     Frags& f) {
-  read_a<BK, SWIGLU, true>(stage, 1, wm, lane, f);
-#pragma unroll
-  for (int j = 0; j < NT; ++j)
-    f.b[j] = dequant8(raw[j][2], raw[j][3], SWIGLU && j >= 2 ? sc.s1 : sc.s0);
+// column tile j of k-step ks, dequantized (W3 tiles take s1 in the up projection)
+template <bool SWIGLU>
+__device__ __forceinline__ void dequant_tile(const u32x4_t (&raw)[NT], int j, int ks, StepScale sc,
+                                             Frags& f) {
+  f.b[j] = dequant8(raw[j][2 * ks], raw[j][2 * ks + 1], SWIGLU && j >= 2 ? sc.s1 : sc.s0);
 }
 
 // The four MFMAs of row block i of one k-step.
@@ -449,13 +439,16 @@ __device__ __forceinline__ void run_tile(int& g, int nk, Issuer<BK, SWIGLU, W8>&
       for (int i = 0; i < MB; ++i) {
         const int grp = 4 * s + i;
         if (s == KS - 1 && i == 2) {
-          // B(g+1), then the fragments of the next step's first k-step
+          // B(g+1), then the fragments of the next step's first k-step (fp8
+          // weights: its codes, dequantized after this and the next group)
           wait_vm_lgkm<(NS - 2) * LOADS>();
           __builtin_amdgcn_s_barrier();
-          if (W8)
-            read_frags_w8_first<BK, SWIGLU>(st[(g + 1) % NS], wm, wn, lane, ss_next, raw, fn);
-          else
+          if (W8) {
+            read_w8_raw<BK, SWIGLU>(st[(g + 1) % NS], wn, lane, raw);
+            read_a<BK, SWIGLU, true>(st[(g + 1) % NS], 0, wm, lane, fn);
+          } else {
             read_frags<BK, SWIGLU>(st[(g + 1) % NS], 0, wm, wn, lane, fn);
+          }
           __builtin_amdgcn_sched_barrier(0);
         }
         mfma_row(i, fc, acc);
@@ -468,11 +461,17 @@ __device__ __forceinline__ void run_tile(int& g, int nk, Issuer<BK, SWIGLU, W8>&
             if (j >= (LOADS * grp) / GROUPS && j < upto) is.load(j, dst, wv);
           if (grp == GROUPS - 1) advance<BK, SWIGLU, W8>(is, a, tt, sc, nk, wv, lane);
         }
-        if (i == 0 && s < KS - 1) {
-          if (W8)
-            read_frags_w8_second<BK, SWIGLU>(cur, wm, lane, ss, raw, fn);
-          else
-            read_frags<BK, SWIGLU>(cur, s + 1, wm, wn, lane, fn);
+        if (W8) {
+          // one column tile's dequantization per group of four MFMAs
+          if (s == 0) {
+            if (i == 0) read_a<BK, SWIGLU, true>(cur, 1, wm, lane, fn);
+            dequant_tile<SWIGLU>(raw, i, 1, ss, fn);
+          } else if (i >= 2) {
+            dequant_tile<SWIGLU>(raw, 2 * (i - 2), 0, ss_next, fn);
+            dequant_tile<SWIGLU>(raw, 2 * (i - 2) + 1, 0, ss_next, fn);
+          }
+        } else if (i == 0 && s < KS - 1) {
+          read_frags<BK, SWIGLU>(cur, s + 1, wm, wn, lane, fn);
         }
         __builtin_amdgcn_sched_barrier(0);
       }
@@ -546,7 +545,10 @@ __global__ __launch_bounds__(NTHR, 1) void gemm_bf16_persist_kernel(GroupedGemmA
   if (W8) {
     tsc = tile_scale<SWIGLU>(args, t, wn);
     ss = step_scale(tsc, 0);
-    read_frags_w8_first<BK, SWIGLU>(st[0], wm, wn, lane, ss, raw, f[0]);
+    read_w8_raw<BK, SWIGLU>(st[0], wn, lane, raw);
+    read_a<BK, SWIGLU, true>(st[0], 0, wm, lane, f[0]);
+#pragma unroll
+    for (int j = 0; j < NT; ++j) dequant_tile<SWIGLU>(raw, j, 0, ss, f[0]);
   } else {
     read_frags<BK, SWIGLU>(st[0], 0, wm, wn, lane, f[0]);
   }
@@ -575,7 +577,7 @@ __global__ __launch_bounds__(NTHR, 1) void gemm_bf16_persist_kernel(GroupedGemmA
   wait_vm_lgkm<0>();
 }
 
-constexpr int LIB_BK = 32, LIB_NS = 4, LIB_NS_W8 = 4;
+constexpr int LIB_BK = 32, LIB_NS = 4, LIB_NS_W8 = 6;
 
 }  // namespace gp
 
