@@ -127,7 +127,7 @@ def time_next_rows(moe, c, dev, counts, events: HipEvents, stream, reps=20):
 
 
 def run_workload(name, steps, warmup, events: HipEvents, extra=False, one_stream=False,
-                 overrides=None):
+                 overrides=None, graph=True):
     import torch
     import datagen
     from datagen.device import upload
@@ -151,24 +151,36 @@ def run_workload(name, steps, warmup, events: HipEvents, extra=False, one_stream
     n_ev = 2 * len(STAGES) * steps
     evs = events.create(n_ev)
 
-    def step(ev_ptr):
+    def step(ev_ptr, stream=main):
         st = L.moe_forward_timed(
             c, P(dev["x"]), P(dev["w_r"]), P(dev["b"]), P(ex["w1"]), P(ex["w3"]), P(ex["w2"]),
             P(ex.get("s1")), P(ex.get("s3")), P(ex.get("s2")), P(sh.get("w1")), P(sh.get("w3")),
             P(sh.get("w2")), P(sh.get("s1")), P(sh.get("s3")), P(sh.get("s2")), out.data_ptr(),
-            None, None, counts.data_ptr(), ws.data_ptr(), ws.numel(), main.cuda_stream,
-            side.cuda_stream, ev_ptr)
+            None, None, counts.data_ptr(), ws.data_ptr(), ws.numel(), stream.cuda_stream,
+            (stream if one_stream else side).cuda_stream, ev_ptr)
         if st != 0:
             raise RuntimeError(f"moe_forward_timed: {moe.status_string(st)}: {moe.last_error()}")
 
     for _ in range(warmup):
         step(None)
     torch.cuda.synchronize()
+    run = lambda: step(None)
+    if graph:
+        # one forward (both streams) captured in a HIP graph, replayed per step
+        g = torch.cuda.CUDAGraph()
+        cap = torch.cuda.Stream()
+        cap.wait_stream(main)
+        with torch.cuda.graph(g, stream=cap, capture_error_mode="relaxed"):
+            step(None, cap)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        run = g.replay
     # the timed steps carry no stage events; the per-stage times come from as
-    # many steps again, each stage bracketed by events on its own stream
+    # many eager steps again, each stage bracketed by events on its own stream
     t_start = time.perf_counter()
     for i in range(steps):
-        step(None)
+        run()
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t_start
     arrays = [ev_arr_t(*evs[i * 2 * len(STAGES):(i + 1) * 2 * len(STAGES)]) for i in range(steps)]
@@ -390,6 +402,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="v3_prefill")
     ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--no-graph", action="store_true",
+                    help="time eager forwards instead of replays of one captured HIP graph")
     ap.add_argument("--no-fp8-prefill", action="store_true",
                     help="skip the V3-shaped prefill with fp8 block-scaled weights")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -409,7 +423,7 @@ def main():
     if args.copy_calibration:
         copy_calibration()
     r = run_workload(args.workload, args.steps, args.warmup, events, extra=True,
-                     one_stream=args.one_stream)
+                     one_stream=args.one_stream, graph=not args.no_graph)
     cfg = r["cfg"]
     value = cfg.T * args.steps / r["elapsed"]
     flops = cfg.flops_per_token() * cfg.T
@@ -418,6 +432,7 @@ def main():
         "value": round(value, 1), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": round(r["ms_per_step"], 4), "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None, "dtype": cfg.w_dtype, "data": "synthetic",
+        "launch": "eager" if args.no_graph else "hip graph replay",
         "config": {"workload": cfg.name, "T": cfg.T, "d": cfg.d, "n_routed": cfg.n_routed,
                    "n_shared": cfg.n_shared, "inter": cfg.inter, "k": cfg.k,
                    "groups": f"{cfg.topk_groups}/{cfg.n_groups}", "gate": cfg.gate},
@@ -430,9 +445,11 @@ def main():
     if not args.no_fp8_prefill:
         line["next_rows"]["fp8_prefill"] = fp8_prefill_summary(
             run_workload("v3_prefill", max(2, args.steps // 2), args.warmup, events,
-                         one_stream=args.one_stream, overrides=FP8_PREFILL))
+                         one_stream=args.one_stream, overrides=FP8_PREFILL,
+                         graph=not args.no_graph))
     if not args.no_decode:
-        d = run_workload("v3_decode", args.steps, args.warmup, events, one_stream=args.one_stream)
+        d = run_workload("v3_decode", args.steps, args.warmup, events, one_stream=args.one_stream,
+                         graph=not args.no_graph)
         d.pop("inputs")
         line["decode"] = decode_summary(d)
     if not args.no_cpu_baseline:

@@ -146,10 +146,6 @@ int run_router(const moe_config* c, const void* x, const float* W_r, const float
     nsplit = router_mfma_splits(c->T, c->d, c->n_routed);
     MOE_HIP_CHECK(launch_router_logits_mfma((const bf16_t*)x, W_r, z, c->T, c->d, c->n_routed,
                                             nsplit, s));
-    if (nsplit > kRouterSelectSplits) {
-      MOE_HIP_CHECK(launch_router_sum_splits(z, nsplit, c->T * (int64_t)c->n_routed, s));
-      nsplit = 1;
-    }
   } else {
     MOE_HIP_CHECK(launch_router_logits_simt(false, x, W_r, z, c->T, c->d, c->n_routed, s));
   }

@@ -7,7 +7,9 @@
 // Idea 2).  Each output element is summed in fp32 in a fixed order - the k
 // routed terms in selection order, then y_shared, then the residual - by the
 // one thread that owns it, so the result does not depend on scheduling.
-// One 256-thread block per token row; each thread owns 8 consecutive columns.
+// A 256-thread block covers 2048 columns of one token row (grid: tokens x
+// column blocks), each thread 8 consecutive columns, so a few tokens (decode)
+// still spread over many CUs.
 #include "moe_internal.h"
 
 namespace moe {
@@ -63,7 +65,8 @@ __global__ __launch_bounds__(256) void combine_kernel(const TA* __restrict__ y_p
     s_g[threadIdx.x] = gate[t * k + threadIdx.x];
   }
   __syncthreads();
-  for (int c = threadIdx.x * 8; c < d; c += 256 * 8) {
+  const int c = blockIdx.y * (256 * 8) + threadIdx.x * 8;
+  if (c < d) {
     float acc[8];
 #pragma unroll
     for (int i = 0; i < 8; ++i) acc[i] = 0.f;
@@ -95,7 +98,7 @@ hipError_t launch_combine(bool act_bf16, bool out_bf16, const void* y_perm,
                           const void* residual, void* out, int64_t T, int d, int k,
                           hipStream_t stream) {
   if (T <= 0) return hipSuccess;
-  const unsigned grid = (unsigned)T;
+  const dim3 grid((unsigned)T, (unsigned)cdiv(d, 256 * 8));
   if (act_bf16 && out_bf16)
     combine_kernel<bf16_t, bf16_t><<<grid, 256, 0, stream>>>(
         (const bf16_t*)y_perm, slot_row, gate, (const bf16_t*)y_shared, (const bf16_t*)residual,

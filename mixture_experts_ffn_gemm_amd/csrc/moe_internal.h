@@ -43,9 +43,7 @@ hipError_t launch_router_logits_simt(bool x_bf16, const void* x, const float* W_
 int router_mfma_splits(int64_t T, int d, int N);
 hipError_t launch_router_logits_mfma(const bf16_t* x, const float* W_r, float* zpart, int64_t T,
                                      int d, int N, int nsplit, hipStream_t stream);
-// zpart[0] = the sum of the nsplit partials in split order (TN = T * N)
-hipError_t launch_router_sum_splits(float* zpart, int nsplit, int64_t TN, hipStream_t stream);
-constexpr int kRouterSelectSplits = 8;  // partials the selection adds itself
+constexpr int kRouterSelectSplits = 16;  // at most this many K splits
 
 // Scores, group-limited top-k and gates from z (the sum of nsplit partials).
 // Experts out of the selection: allow bit e of word e/64 (when `any`), then

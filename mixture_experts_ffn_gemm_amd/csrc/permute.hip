@@ -12,24 +12,18 @@
 //   2. scan:    one block per expert scans the chunk counts -> per-chunk base
 //               and the expert's total;
 //   3. scatter: row = offset[e] + base[chunk][e] + rank; row_token / slot_row.
+// Up to four chunks (decode) run all three steps in one block.
 // Rows are ordered by expert, then by slot index f = t*k + j (stable).
 #include "moe_internal.h"
 #include "wave_utils.h"
 
 namespace moe {
 
-__global__ __launch_bounds__(256) void permute_hist_kernel(const int32_t* __restrict__ idx,
-                                                           int64_t S, int N, int nchunks,
-                                                           int32_t* __restrict__ hist,
-                                                           int32_t* __restrict__ rank) {
-  extern __shared__ int cnt_all[];  // 4 * N
-  const int w = threadIdx.x >> 6, lane = lane_id();
-  const int c = blockIdx.x * 4 + w;
-  int* cnt = cnt_all + w * N;
-  for (int i = lane; i < N; i += 64) cnt[i] = 0;
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
-  __builtin_amdgcn_wave_barrier();
-  if (c >= nchunks) return;
+// Wavefront-level: counts of chunk c's experts into cnt (LDS, N entries,
+// zeroed) and each slot's rank among the equal experts of the chunk.
+__device__ __forceinline__ void rank_chunk(const int32_t* __restrict__ idx, int64_t S, int c,
+                                           int* cnt, int32_t* rank) {
+  const int lane = lane_id();
   const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
   for (int it = 0; it < kPermChunk / 64; ++it) {
     const int64_t f = (int64_t)c * kPermChunk + it * 64 + lane;
@@ -52,7 +46,65 @@ __global__ __launch_bounds__(256) void permute_hist_kernel(const int32_t* __rest
     __builtin_amdgcn_wave_barrier();
     if (valid) rank[f] = base + before;
   }
+}
+
+__global__ __launch_bounds__(256) void permute_hist_kernel(const int32_t* __restrict__ idx,
+                                                           int64_t S, int N, int nchunks,
+                                                           int32_t* __restrict__ hist,
+                                                           int32_t* __restrict__ rank) {
+  extern __shared__ int cnt_all[];  // 4 * N
+  const int w = threadIdx.x >> 6, lane = lane_id();
+  const int c = blockIdx.x * 4 + w;
+  int* cnt = cnt_all + w * N;
+  for (int i = lane; i < N; i += 64) cnt[i] = 0;
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+  __builtin_amdgcn_wave_barrier();
+  if (c >= nchunks) return;
+  rank_chunk(idx, S, c, cnt, rank);
   for (int i = lane; i < N; i += 64) hist[(int64_t)c * N + i] = cnt[i];
+}
+
+// A few slots (decode: S <= 4 chunks): one block does all three steps, wave w
+// ranking chunk w, with the counts and ranks kept in LDS.
+__global__ __launch_bounds__(256) void permute_small_kernel(
+    const int32_t* __restrict__ idx, int64_t S, int k, int N, int nchunks,
+    int32_t* __restrict__ counts, int32_t* __restrict__ offsets, int32_t* __restrict__ row_token,
+    int32_t* __restrict__ slot_row) {
+  __shared__ int cnt[4][256];            // per chunk, then the chunk's base per expert
+  __shared__ int rank_s[4 * kPermChunk];
+  __shared__ int s_off[257];
+  __shared__ int scratch[4];
+  const int tid = threadIdx.x, w = tid >> 6;
+  for (int i = tid; i < 4 * 256; i += 256) cnt[i >> 8][i & 255] = 0;
+  __syncthreads();
+  if (w < nchunks) rank_chunk(idx, S, w, cnt[w], rank_s);
+  __syncthreads();
+  int v = 0;
+  if (tid < N) {
+    for (int c = 0; c < nchunks; ++c) {
+      const int x = cnt[c][tid];
+      cnt[c][tid] = v;
+      v += x;
+    }
+  }
+  int tot;
+  const int incl = block_incl_scan<256>(v, scratch, &tot);
+  if (tid < N) {
+    s_off[tid] = incl - v;
+    counts[tid] = v;
+    offsets[tid] = incl - v;
+  }
+  if (tid == 0) {
+    s_off[N] = tot;
+    offsets[N] = tot;
+  }
+  __syncthreads();
+  for (int64_t f = tid; f < S; f += 256) {
+    const int e = idx[f];
+    const int row = s_off[e] + cnt[f / kPermChunk][e] + rank_s[f];
+    row_token[row] = (int32_t)(f / k);
+    slot_row[f] = row;
+  }
 }
 
 __global__ __launch_bounds__(256) void permute_scan_kernel(const int32_t* __restrict__ hist,
@@ -106,6 +158,11 @@ hipError_t launch_permute(const int32_t* idx, int64_t T, int k, int N, int32_t* 
                           int32_t* row_token, int32_t* slot_row, hipStream_t stream) {
   const int64_t S = T * k;
   const int nchunks = (int)cdiv(S, kPermChunk);
+  if (nchunks <= 4) {
+    permute_small_kernel<<<1, 256, 0, stream>>>(idx, S, k, N, nchunks, counts, offsets, row_token,
+                                                slot_row);
+    return hipGetLastError();
+  }
   permute_hist_kernel<<<(unsigned)cdiv(nchunks, 4), 256, 4 * N * sizeof(int), stream>>>(
       idx, S, N, nchunks, hist, rank);
   permute_scan_kernel<<<N, 256, 0, stream>>>(hist, nchunks, N, base, counts);

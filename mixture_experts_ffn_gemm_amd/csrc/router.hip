@@ -229,44 +229,22 @@ __global__ __launch_bounds__(256, 1) void router_logits_mfma_kernel(
     }
 }
 
-// About 512 blocks in all, each with at least two K tiles; the partial sums
-// (added in split order by the selection kernel) take at most 64 MiB.  A few
-// tokens (decode) thus spread over many blocks: a block's K loop waits for
-// one load per tile, so fewer tiles per block is what makes it fast.
+// About 512 blocks in all, each with at least two K tiles, and at most
+// kRouterSelectSplits partials (added in split order by the selection kernel,
+// at most 64 MiB of them).  A few tokens (decode) thus spread over many
+// blocks: a block's K loop waits for one load per tile, so fewer tiles per
+// block is what makes it fast.
 int router_mfma_splits(int64_t T, int d, int N) {
   const int64_t tiles = cdiv(T, 128) * cdiv(N, 128);
   if (tiles <= 0) return 1;
   const int nk = d / 64;
   int64_t s = cdiv(512, tiles);
   if (s > nk / 2) s = nk / 2;
+  if (s > kRouterSelectSplits) s = kRouterSelectSplits;
   const int64_t per_split = T * (int64_t)N * 4;
   if (s * per_split > (int64_t(64) << 20)) s = (int64_t(64) << 20) / per_split;
   if (s < 1) s = 1;
   return (int)s;
-}
-
-// Many splits (a few tokens): the partials are first added in split order
-// into split 0, one thread per logit, so the selection reads one value.
-__global__ __launch_bounds__(256) void router_sum_splits_kernel(float* __restrict__ z, int nsplit,
-                                                                int64_t TN) {
-  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (i >= TN) return;
-  float s = 0.f;
-  for (int s0 = 0; s0 < nsplit; s0 += 8) {
-    // eight independent loads in flight, then the adds in split order
-    float part[8];
-#pragma unroll
-    for (int sp = 0; sp < 8; ++sp) part[sp] = s0 + sp < nsplit ? z[(s0 + sp) * TN + i] : 0.f;
-#pragma unroll
-    for (int sp = 0; sp < 8; ++sp)
-      if (s0 + sp < nsplit) s += part[sp];
-  }
-  z[i] = s;
-}
-
-hipError_t launch_router_sum_splits(float* z, int nsplit, int64_t TN, hipStream_t stream) {
-  router_sum_splits_kernel<<<(unsigned)cdiv(TN, 256), 256, 0, stream>>>(z, nsplit, TN);
-  return hipGetLastError();
 }
 
 hipError_t launch_router_logits_mfma(const bf16_t* x, const float* W_r, float* zpart, int64_t T,
@@ -301,23 +279,33 @@ __global__ __launch_bounds__(256) void router_select_kernel(
 
   float val[kSelPerLane], key[kSelPerLane];
   bool ok[kSelPerLane];
+  // the split partials of the lane's experts, 8 splits at a time (all loads
+  // of a round in flight together), added in split order
+  float zsum[kSelPerLane];
+#pragma unroll
+  for (int j = 0; j < kSelPerLane; ++j) {
+    ok[j] = lane + 64 * j < N;
+    zsum[j] = 0.f;
+  }
+  for (int s0 = 0; s0 < nsplit; s0 += 8) {
+    float part[kSelPerLane][8];
+#pragma unroll
+    for (int j = 0; j < kSelPerLane; ++j)
+#pragma unroll
+      for (int sp = 0; sp < 8; ++sp)
+        part[j][sp] = ok[j] && s0 + sp < nsplit
+                          ? z[((int64_t)(s0 + sp) * T + t) * N + lane + 64 * j]
+                          : 0.f;
+#pragma unroll
+    for (int j = 0; j < kSelPerLane; ++j)
+#pragma unroll
+      for (int sp = 0; sp < 8; ++sp)
+        if (s0 + sp < nsplit) zsum[j] += part[j][sp];
+  }
 #pragma unroll
   for (int j = 0; j < kSelPerLane; ++j) {
     const int e = lane + 64 * j;
-    ok[j] = e < N;
-    float zz = 0.f;
-    if (ok[j]) {
-      // the split partials, 8 loads at a time, added in split order
-      for (int s0 = 0; s0 < nsplit; s0 += 8) {
-        float part[8];
-#pragma unroll
-        for (int sp = 0; sp < 8; ++sp)
-          part[sp] = s0 + sp < nsplit ? z[((int64_t)(s0 + sp) * T + t) * N + e] : 0.f;
-#pragma unroll
-        for (int sp = 0; sp < 8; ++sp)
-          if (s0 + sp < nsplit) zz += part[sp];
-      }
-    }
+    const float zz = zsum[j];
     const float bb = (ok[j] && b) ? b[e] : 0.f;
     val[j] = zz + bb;  // softmax: biased logit; overwritten below for sigmoid
     key[j] = bb;

@@ -368,6 +368,37 @@ def test_forward_fp8_prefill(lib):
     assert torch.equal(a, b)
 
 
+@pytest.mark.parametrize("name", ["v3_decode", "v3_prefill"])
+def test_forward_graph_replay(lib, name):
+    """The forward, with its shared expert on a side stream, captured in a HIP
+    graph and replayed three times with eager forwards in between: every
+    replay and every eager forward equals the first eager result bitwise."""
+    cfg = small_cfg(name)
+    say(f"[forward-graph] {name} T={cfg.T}")
+    dev = upload(datagen.MoEInputs(cfg))
+    c = lib.config_from(cfg)
+    side = torch.cuda.Stream()
+    args = (c, dev["x"], dev["w_r"], dev["b"], dev["experts"], dev["shared"])
+    ref = lib.forward(*args, side_stream=side).clone()
+    torch.cuda.synchronize()
+    out = torch.empty_like(ref)
+    g = torch.cuda.CUDAGraph()
+    cap = torch.cuda.Stream()
+    cap.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.graph(g, stream=cap, capture_error_mode="relaxed"):
+        lib.forward(*args, out=out, side_stream=side)
+    torch.cuda.synchronize()
+    for r in range(3):
+        out.zero_()
+        eager = lib.forward(*args, side_stream=side)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        say(f"   replay {r}: equal {torch.equal(out, ref)}, eager equal {torch.equal(eager, ref)}")
+        assert torch.equal(out, ref)
+        assert torch.equal(eager, ref)
+
+
 def test_forward_deterministic_and_bf16_out(lib):
     cfg = small_cfg("v3_prefill")
     say("[determinism] v3 small, two runs + bf16 output")
