@@ -183,7 +183,8 @@ int moe_permute(const moe_config* cfg, const int32_t* topk_idx, const void* x,
  * Experts with no rows are never read.  fp8 weights: with at least 128 rows
  * per expert on average (max_rows >= 128 * n_experts) the codes are
  * dequantized to bf16(code * scale) for bf16 MFMAs (prefill); with fewer, each
- * expert's weights are streamed once and multiplied exactly in fp32 (decode).
+ * expert's weights are streamed once, the codes multiplied exactly and each
+ * 128-wide block's fp32 partial sum scaled once (decode).
  */
 int moe_expert_ffn(const moe_config* cfg, int32_t n_experts, const int32_t* offsets,
                    int64_t max_rows, int32_t inter_override,
