@@ -389,7 +389,64 @@ def summarize_pmc(fetch_csv, write_csv, command):
     print(header + json.dumps(db, indent=1))
 
 
+def summarize_util(csv_path, command, out_path):
+    """MFMA utilisation, clock and LDS bank conflicts per launch of the main
+    GEMMs from one rocprofv3 --pmc run (GRBM_GUI_ACTIVE, SQ_BUSY_CYCLES,
+    SQ_VALU_MFMA_BUSY_CYCLES, SQ_LDS_BANK_CONFLICT, SQ_LDS_IDX_ACTIVE).
+    rocprofv3 reports each counter summed over its hardware instances; the
+    GPU-busy cycles GRBM_GUI_ACTIVE come from one instance per XCD."""
+    import collections
+    import csv
+    per = collections.defaultdict(lambda: collections.defaultdict(float))
+    names, dur = {}, {}
+    for r in csv.DictReader(open(csv_path)):
+        key = (r["Kernel_Name"], int(r["Grid_Size"]), int(r["Dispatch_Id"]))
+        per[key][r["Counter_Name"]] += float(r["Counter_Value"])
+        names[key] = r["Kernel_Name"]
+        dur[key] = int(r["End_Timestamp"]) - int(r["Start_Timestamp"])
+    n_xcd, simds = 8, 256 * 4
+    targets = {"bf16 routed up (prefill)": "gemm_bf16_persist_kernel<32, 4, true, false>",
+               "bf16 routed down (prefill)": "gemm_bf16_persist_kernel<32, 4, false, false>",
+               "fp8-weight routed up (prefill)": "gemm_bf16_persist_kernel<32, 6, true, true>",
+               "fp8 routed up (decode)": "gemm_fp8_small_kernel<true, 4, 2>"}
+    lines = ["# MFMA utilisation of the main GEMM launches (rocprofv3 --pmc, one run)",
+             "# command (run from /tmp, TMPDIR=/tmp):",
+             f"#   {command}",
+             "# summary: python bench.py --summarize-util <out>/bench_counter_collection.csv '<command>' <this file>",
+             "# per kernel, its routed launches (largest grid, at least half the longest duration) averaged:",
+             "#   cycles = GRBM_GUI_ACTIVE / 8 XCDs;",
+             "#   clock = cycles / launch duration; mfma_busy = SQ_VALU_MFMA_BUSY_CYCLES / (cycles x 1024 SIMDs);",
+             "#   lds_conflict = SQ_LDS_BANK_CONFLICT / SQ_LDS_IDX_ACTIVE",
+             f"{'launch':34s} {'dispatches':>10s} {'ms':>8s} {'clock_GHz':>10s} {'mfma_busy':>10s} "
+             f"{'lds_conflict':>13s}"]
+    for label, pat in targets.items():
+        keys = [k for k in per if pat in names[k]]
+        if not keys:
+            continue
+        gmax = max(k[1] for k in keys)
+        keys = [k for k in keys if k[1] == gmax]
+        # the persistent grid is the same for the routed and the shared
+        # launches; the routed ones run several times longer
+        dmax = max(dur[k] for k in keys)
+        keys = [k for k in keys if dur[k] >= 0.5 * dmax]
+        n = len(keys)
+        cyc = sum(per[k]["GRBM_GUI_ACTIVE"] for k in keys) / n / n_xcd
+        ms = sum(dur[k] for k in keys) / n / 1e6
+        mf = sum(per[k]["SQ_VALU_MFMA_BUSY_CYCLES"] for k in keys) / n
+        lc = sum(per[k]["SQ_LDS_BANK_CONFLICT"] for k in keys)
+        la = sum(per[k]["SQ_LDS_IDX_ACTIVE"] for k in keys)
+        lines.append(f"{label:34s} {n:10d} {ms:8.3f} {cyc / (ms * 1e6):10.2f} {mf / (cyc * simds):10.3f} "
+                     f"{(lc / la if la else 0.0):13.4f}")
+    text = "\n".join(lines) + "\n"
+    with open(out_path, "w") as f:
+        f.write(text)
+    print(text)
+
+
 def main():
+    if len(sys.argv) > 1 and sys.argv[1] == "--summarize-util":
+        summarize_util(sys.argv[2], sys.argv[3], sys.argv[4])
+        return
     if len(sys.argv) > 1 and sys.argv[1] == "--summarize-trace":
         summarize_trace(sys.argv[2], sys.argv[3] if len(sys.argv) > 3 else "")
         return
