@@ -17,16 +17,18 @@
 // count are skipped.  Experts without rows own no tile and are never read.
 //
 // Streaming.  The weights go straight from HBM into a per-lane register ring
-// PF k-blocks deep; a k-block's weights are converted to bf16 before the ring
-// slot is refilled, so the compiler never copies a register a load is still
-// writing.  The activations (a few rows, L2-resident) are read once per
+// PF k-blocks deep, by non-temporal loads of whole 128-byte lines (a DPP lane
+// rotate puts each lane's pieces in MFMA order); a k-block's weights are
+// converted to bf16 before the ring slot is refilled, so the compiler never
+// copies a register a load is still writing.  The activations (a few rows, L2-resident) are read once per
 // workgroup, not once per wavefront: each thread loads its 16-byte pieces
 // into a small register ring, writes them to one of two LDS slots a k-block
 // ahead, and one barrier per k-block publishes them.  Every load is issued
 // unconditionally (past the end it repeats the last k-block), so the code is
 // straight-line and the compiler's wait counts keep the whole ring in flight.
 // With activations read once per wavefront instead, the extra loads cost
-// 25-45% of the streaming rate.
+// 25-45% of the streaming rate; with ordinary loads of half lines (the
+// natural MFMA order) the weights stream about 10% slower.
 #include <type_traits>
 
 #include "grouped_sched.h"
@@ -57,6 +59,24 @@ __device__ __forceinline__ bf16x8_t fp8x8_to_bf16(uint32_t w0, uint32_t w1) {
   return bf16x8_t{p0[0], p0[1], p1[0], p1[1], p2[0], p2[1], p3[0], p3[1]};
 }
 
+// Lane L = (kg << 4) | col of an MFMA B operand needs, for the 64-wide half h
+// of a k-block, the 16-byte piece 4h + kg of column col.  Load i holds, in lane
+// (kg << 4) | (hh << 3) | c, piece 4hh + kg of column 8i + c; so lanes whose bit
+// 3 equals h keep load h's value, and the others take load 1-h's value from
+// lane L ^ 8 (a DPP rotate by 8 within the 16-lane row, written to the two
+// banks of 4 lanes that have bit 3 != h).
+__device__ __forceinline__ u32x4_t ring_to_mfma(const u32x4_t (&ld)[2], int h) {
+  constexpr int kRowRor8 = 0x128;
+  u32x4_t r;
+#pragma unroll
+  for (int d = 0; d < 4; ++d)
+    r[d] = h == 0 ? (uint32_t)__builtin_amdgcn_update_dpp((int)ld[0][d], (int)ld[1][d], kRowRor8, 0xf,
+                                                          0xc, false)
+                  : (uint32_t)__builtin_amdgcn_update_dpp((int)ld[1][d], (int)ld[0][d], kRowRor8, 0xf,
+                                                          0x3, false);
+  return r;
+}
+
 template <int P, int N, class F>
 __device__ __forceinline__ void static_for(F&& f) {
   if constexpr (P < N) {
@@ -83,24 +103,27 @@ __device__ __forceinline__ void tile(const GroupedGemmArgs& args, const TileCoor
   const int K = args.K, Nout = args.Nout, KB = K / 128;  // KB % PF == 0
   const int ncol0 = tc.n0 + wv * 16;
 
-  const uint8_t* bp[NB];
+  // Weights: two loads per k-block and matrix, each reading 8 whole 128-byte
+  // lines (columns 8i .. 8i+7 of the wave): lane l takes column 8i + (l & 7),
+  // 16-byte piece 4*((l >> 3) & 1) + (l >> 4).  Non-temporal: each line is read
+  // once.  A DPP rotate by 8 lanes then gives every lane the pieces of its
+  // MFMA column (see ring_to_mfma).
+  const uint8_t* bp[NB];  // load i of a k-block reads 8 rows (8 * K bytes) further
   cfloat* sp[NB];
   {
-    int n = ncol0 + col;
-    if (n > Nout - 1) n = Nout - 1;
     // the shared expert folded in as the last group has weights of its own
     const bool xg = args.B0x && tc.group == args.n_groups - 1;
     const int g = xg ? 0 : __builtin_amdgcn_readfirstlane(tc.group);
-    const int64_t boff = ((int64_t)g * Nout + n) * K + kg * 16;
+    const int piece = 4 * ((lane >> 3) & 1) + (lane >> 4);
+    // Nout is a multiple of 128, so all 64 columns of a tile exist
+    const int64_t boff = ((int64_t)g * Nout + ncol0 + (lane & 7)) * K + piece * 16;
+    bp[0] = (const uint8_t*)(xg ? args.B0x : args.B0) + boff;
+    if (SWIGLU) bp[NB - 1] = (const uint8_t*)(xg ? args.B1x : args.B1) + boff;
     // the wave's 16 columns lie in one 128-column scale block: scalar loads
     const int nb = __builtin_amdgcn_readfirstlane((ncol0 < Nout ? ncol0 : Nout - 1) >> 7);
     const int64_t soff = ((int64_t)g * (Nout / 128) + nb) * KB;
-    bp[0] = (const uint8_t*)(xg ? args.B0x : args.B0) + boff;
     sp[0] = (cfloat*)((xg ? args.S0x : args.S0) + soff);
-    if (SWIGLU) {
-      bp[NB - 1] = (const uint8_t*)(xg ? args.B1x : args.B1) + boff;
-      sp[NB - 1] = (cfloat*)((xg ? args.S1x : args.S1) + soff);
-    }
+    if (SWIGLU) sp[NB - 1] = (cfloat*)((xg ? args.S1x : args.S1) + soff);
   }
   // Activation staging: in chunk c, wave wv fills LDS rows 4wv .. 4wv+3 of
   // a slot; lane l writes row 4wv + (l >> 4), 16-byte position l & 15, with
@@ -147,7 +170,9 @@ __device__ __forceinline__ void tile(const GroupedGemmArgs& args, const TileCoor
 #pragma unroll
     for (int m = 0; m < NB; ++m)
 #pragma unroll
-      for (int h = 0; h < 2; ++h) ring[p][m][h] = *(const u32x4_t*)(bp[m] + kp * 128 + h * 64);
+      for (int i = 0; i < 2; ++i)
+        ring[p][m][i] =
+            __builtin_nontemporal_load((const u32x4_t*)(bp[m] + (int64_t)i * 8 * K + kp * 128));
   };
   // prologue: A(0) to LDS slot 0, A(1 .. RA) into the register ring, the
   // weights of k-blocks 0 .. PF-1 in flight
@@ -175,8 +200,9 @@ __device__ __forceinline__ void tile(const GroupedGemmArgs& args, const TileCoor
       for (int m = 0; m < NB; ++m)
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
-          wb[m][h][0] = fp8x8_to_bf16(ring[p][m][h][0], ring[p][m][h][1]);
-          wb[m][h][1] = fp8x8_to_bf16(ring[p][m][h][2], ring[p][m][h][3]);
+          const u32x4_t w = ring_to_mfma(ring[p][m], h);
+          wb[m][h][0] = fp8x8_to_bf16(w[0], w[1]);
+          wb[m][h][1] = fp8x8_to_bf16(w[2], w[3]);
         }
       load_w(p, kb + PF);
       __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): this thread's LDS writes
@@ -257,7 +283,7 @@ __global__ __launch_bounds__(256, LB) void gemm_fp8_small_kernel(GroupedGemmArgs
 }  // namespace f8
 
 // Up: W1 and W3 streams, a ring of 4 k-blocks, two workgroups per CU.  Down:
-// one stream over a short K (= I), a ring of 2 k-blocks and four workgroups
+// one stream over a short K (= I), a ring of 2 k-blocks and three workgroups
 // per CU, whose start-up latencies (tile lookup, row indices) then overlap
 // each other's streams.  K / 128 not a multiple of the ring: a ring of 1.
 hipError_t launch_gemm_fp8_swiglu(const GroupedGemmArgs& a, hipStream_t s) {
@@ -274,9 +300,9 @@ hipError_t launch_gemm_fp8_store(const GroupedGemmArgs& a, hipStream_t s) {
   const int64_t grid = grouped_grid(a.max_rows, a.n_groups, f8::BM, f8::BN, a.Nout);
   if (grid <= 0) return hipSuccess;
   if ((a.K / 128) % 2 == 0)
-    f8::gemm_fp8_small_kernel<false, 2, 4><<<(unsigned)grid, 256, 0, s>>>(a);
+    f8::gemm_fp8_small_kernel<false, 2, 3><<<(unsigned)grid, 256, 0, s>>>(a);
   else
-    f8::gemm_fp8_small_kernel<false, 1, 4><<<(unsigned)grid, 256, 0, s>>>(a);
+    f8::gemm_fp8_small_kernel<false, 1, 3><<<(unsigned)grid, 256, 0, s>>>(a);
   return hipGetLastError();
 }
 
