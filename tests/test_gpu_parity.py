@@ -154,7 +154,8 @@ def test_router_zero_weights_tie_break(lib):
 
 @pytest.mark.parametrize("T,k,N,skew", [(1, 1, 1, False), (3, 2, 16, False), (1000, 7, 63, False),
                                         (4097, 8, 256, False), (700, 6, 160, True),
-                                        (64, 8, 256, True)])
+                                        (64, 8, 256, True), (128, 8, 256, False),
+                                        (129, 8, 256, True), (1, 8, 8, False)])
 def test_permute_bit_exact(lib, T, k, N, skew):
     say(f"[permute] T={T} k={k} N={N} skew={skew}")
     rng = np.random.default_rng(T * 31 + N)
