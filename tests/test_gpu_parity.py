@@ -270,10 +270,14 @@ def test_expert_ffn_ragged_groups(lib, wdt):
 # ---------------------------------------------------------------- combine
 
 
-@pytest.mark.parametrize("act,out", [("bf16", "f32"), ("bf16", "bf16"), ("f32", "f32")])
-def test_combine(lib, act, out):
-    T, d, k = 333, 384, 6
-    say(f"[combine] act={act} out={out}")
+# k <= 8 runs a kernel specialised for that k, k > 8 the generic one (batches of 8)
+@pytest.mark.parametrize("act,out,k,d", [("bf16", "f32", 6, 384), ("bf16", "bf16", 6, 384),
+                                         ("f32", "f32", 6, 384), ("f32", "bf16", 3, 384),
+                                         ("bf16", "f32", 8, 2560), ("bf16", "f32", 11, 2560),
+                                         ("f32", "f32", 1, 192)])
+def test_combine(lib, act, out, k, d):
+    T = 333
+    say(f"[combine] act={act} out={out} k={k} d={d}")
     rng = np.random.default_rng(5)
     tdt = torch.bfloat16 if act == "bf16" else torch.float32
     y_perm = torch.from_numpy(rng.standard_normal((T * k, d)).astype(np.float32)).to(tdt).cuda()
