@@ -43,7 +43,7 @@ hipError_t launch_router_logits_simt(bool x_bf16, const void* x, const float* W_
 int router_mfma_splits(int64_t T, int d, int N);
 hipError_t launch_router_logits_mfma(const bf16_t* x, const float* W_r, float* zpart, int64_t T,
                                      int d, int N, int nsplit, hipStream_t stream);
-constexpr int kRouterSelectSplits = 16;  // at most this many K splits
+constexpr int kRouterSelectSplits = 64;  // at most this many K splits
 
 // Scores, group-limited top-k and gates from z (the sum of nsplit partials).
 // Experts out of the selection: allow bit e of word e/64 (when `any`), then

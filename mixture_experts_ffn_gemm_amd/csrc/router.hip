@@ -268,45 +268,80 @@ __device__ __forceinline__ int unpack_idx(uint64_t p) {
   return (int)(0xffffffffu - (uint32_t)(p & 0xffffffffu));
 }
 
+// R > 0 (N % 4 == 0): lane l adds the partials of experts 4l .. 4l+3 with
+// 16-byte loads, R splits in flight at a time, and the sums go through LDS to
+// the lanes that select.  R == 0: one expert per load, 8 splits at a time.
+// Either way each expert's partials are added in split order, starting from 0.
+template <int R>
 __global__ __launch_bounds__(256) void router_select_kernel(
     const float* __restrict__ z, int nsplit, const float* __restrict__ b, int64_t T, int N, int k,
     int n_groups, int topk_groups, int group_topn, int gate, float route_scale, ExpertMask mask,
     int32_t* __restrict__ out_idx, float* __restrict__ out_gate, float* __restrict__ scores) {
   const int lane = lane_id();
-  const int64_t t = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int wv = threadIdx.x >> 6;
+  const int64_t t = (int64_t)blockIdx.x * 4 + wv;
   if (t >= T) return;  // uniform per wavefront
   const float NEG_INF = -__builtin_inff();
 
   float val[kSelPerLane], key[kSelPerLane];
   bool ok[kSelPerLane];
-  // the split partials of the lane's experts, 8 splits at a time (all loads
-  // of a round in flight together), added in split order
-  float zsum[kSelPerLane];
+  // the bias first (a missing bias reads z and is not used), so that its
+  // loads overlap those of the partials
+  float bias[kSelPerLane];
+  const float* bsrc = b ? b : z;
 #pragma unroll
   for (int j = 0; j < kSelPerLane; ++j) {
     ok[j] = lane + 64 * j < N;
-    zsum[j] = 0.f;
+    bias[j] = bsrc[ok[j] ? lane + 64 * j : 0];
   }
-  for (int s0 = 0; s0 < nsplit; s0 += 8) {
-    float part[kSelPerLane][8];
+  float zsum[kSelPerLane];
+  if (R > 0) {
+    __shared__ __attribute__((aligned(16))) float sums[4][256];
+    // lanes past the last expert read experts 0..3 and drop them
+    const float* zp = z + t * N + (4 * lane < N ? 4 * lane : 0);
+    const int64_t sstride = T * (int64_t)N;
+    f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+    for (int s0 = 0; s0 < nsplit; s0 += (R > 0 ? R : 1)) {
+      f32x4_t part[R > 0 ? R : 1];
 #pragma unroll
-    for (int j = 0; j < kSelPerLane; ++j)
+      for (int sp = 0; sp < R; ++sp) {  // clamped, so that no load is conditional
+        const int sx = s0 + sp < nsplit ? s0 + sp : nsplit - 1;
+        part[sp] = *(const f32x4_t*)(zp + sx * sstride);
+      }
+      __builtin_amdgcn_sched_barrier(0);  // all R loads before the first add
 #pragma unroll
-      for (int sp = 0; sp < 8; ++sp)
-        part[j][sp] = ok[j] && s0 + sp < nsplit
-                          ? z[((int64_t)(s0 + sp) * T + t) * N + lane + 64 * j]
-                          : 0.f;
+      for (int sp = 0; sp < R; ++sp) {
+        const f32x4_t a = acc + part[sp];
+        acc = s0 + sp < nsplit ? a : acc;
+      }
+    }
+    *(f32x4_t*)&sums[wv][4 * lane] = acc;  // this wavefront's row only
 #pragma unroll
-    for (int j = 0; j < kSelPerLane; ++j)
+    for (int j = 0; j < kSelPerLane; ++j) zsum[j] = sums[wv][lane + 64 * j];
+  } else {
 #pragma unroll
-      for (int sp = 0; sp < 8; ++sp)
-        if (s0 + sp < nsplit) zsum[j] += part[j][sp];
+    for (int j = 0; j < kSelPerLane; ++j) zsum[j] = 0.f;
+    for (int s0 = 0; s0 < nsplit; s0 += 8) {
+      float part[kSelPerLane][8];
+#pragma unroll
+      for (int j = 0; j < kSelPerLane; ++j)
+#pragma unroll
+        for (int sp = 0; sp < 8; ++sp)
+          part[j][sp] = ok[j] && s0 + sp < nsplit
+                            ? z[((int64_t)(s0 + sp) * T + t) * N + lane + 64 * j]
+                            : 0.f;
+#pragma unroll
+      for (int j = 0; j < kSelPerLane; ++j)
+#pragma unroll
+        for (int sp = 0; sp < 8; ++sp)
+          if (s0 + sp < nsplit) zsum[j] += part[j][sp];
+    }
   }
 #pragma unroll
   for (int j = 0; j < kSelPerLane; ++j) {
     const int e = lane + 64 * j;
     const float zz = zsum[j];
-    const float bb = (ok[j] && b) ? b[e] : 0.f;
+    const float bb = (ok[j] && b) ? bias[j] : 0.f;
     val[j] = zz + bb;  // softmax: biased logit; overwritten below for sigmoid
     key[j] = bb;
     if (gate == 1) {
@@ -451,9 +486,16 @@ hipError_t launch_router_select(const float* z, int nsplit, const float* b, int6
                                 hipStream_t stream, const ExpertMask* mask) {
   const unsigned blocks = (unsigned)cdiv(T, 4);
   const ExpertMask m = mask ? *mask : ExpertMask{};
-  router_select_kernel<<<blocks, 256, 0, stream>>>(z, nsplit, b, T, N, k, n_groups, topk_groups,
-                                                   group_topn, gate, route_scale, m, idx, gates,
-                                                   scores);
+  const bool vec = N % 4 == 0 && ((uintptr_t)z & 15) == 0;
+#define MOE_SELECT(R)                                                                          \
+  router_select_kernel<R><<<blocks, 256, 0, stream>>>(z, nsplit, b, T, N, k, n_groups,         \
+                                                      topk_groups, group_topn, gate,           \
+                                                      route_scale, m, idx, gates, scores)
+  if (!vec) MOE_SELECT(0);
+  else if (nsplit <= 2) MOE_SELECT(2);
+  else if (nsplit <= 8) MOE_SELECT(8);
+  else MOE_SELECT(32);
+#undef MOE_SELECT
   return hipGetLastError();
 }
 
