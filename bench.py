@@ -126,6 +126,9 @@ def time_next_rows(moe, c, dev, counts, events: HipEvents, stream, reps=20):
     return out
 
 
+WARM_S = 0.5  # seconds of back-to-back forwards before the timed ones
+
+
 def run_workload(name, steps, warmup, events: HipEvents, extra=False, one_stream=False,
                  overrides=None, graph=True):
     import torch
@@ -176,6 +179,20 @@ def run_workload(name, steps, warmup, events: HipEvents, extra=False, one_stream
         g.replay()
         torch.cuda.synchronize()
         run = g.replay
+    # Sustained-load warm-up before the timed steps: at least `warmup` more
+    # forwards and at least WARM_S seconds of back-to-back ones.  A kernel trace
+    # of replayed decode forwards after the idle gap of graph capture shows
+    # forwards slowing from 1.20 to 1.46 ms and settling at 1.13-1.15 ms after
+    # about 15 of them (clocks adjusting to the load), which a fixed count of
+    # a few steps does not cover.
+    t_w = time.perf_counter()
+    n_w = 0
+    while n_w < warmup or time.perf_counter() - t_w < WARM_S:
+        run()
+        n_w += 1
+        if n_w % 8 == 0:
+            torch.cuda.synchronize()  # keep the host's clock on the GPU's
+    torch.cuda.synchronize()
     # the timed steps carry no stage events; the per-stage times come from as
     # many eager steps again, each stage bracketed by events on its own stream
     t_start = time.perf_counter()
