@@ -129,6 +129,24 @@ def time_next_rows(moe, c, dev, counts, events: HipEvents, stream, reps=20):
 WARM_S = 0.5  # seconds of back-to-back forwards before the timed ones
 
 
+def gpu_sclk_mhz():
+    """The GPU's current shader clock in MHz as rocm-smi reports it, or None."""
+    import shutil
+    import subprocess
+    exe = shutil.which("rocm-smi") or "/opt/rocm/bin/rocm-smi"
+    try:
+        r = subprocess.run([exe, "--showclocks", "--json"], capture_output=True, text=True,
+                           timeout=20)
+        d = json.loads(r.stdout)
+        for card in d.values():
+            for k, v in card.items():
+                if "sclk" in k.lower() and "speed" in k.lower():
+                    return int(float(str(v).strip("()Mhz ").split()[0]))
+    except Exception:
+        return None
+    return None
+
+
 def run_workload(name, steps, warmup, events: HipEvents, extra=False, one_stream=False,
                  overrides=None, graph=True):
     import torch
@@ -195,11 +213,26 @@ def run_workload(name, steps, warmup, events: HipEvents, extra=False, one_stream
     torch.cuda.synchronize()
     # the timed steps carry no stage events; the per-stage times come from as
     # many eager steps again, each stage bracketed by events on its own stream
+    # one event after each timed step on the stream the steps run on: the
+    # per-step median and spread (the host clock gives the total)
+    tev = events.create(steps + 1)
+    rec = events.hip.hipEventRecord
+    rec.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+    sclk0 = gpu_sclk_mhz()
     t_start = time.perf_counter()
+    rec(tev[0], main.cuda_stream)
     for i in range(steps):
         run()
+        rec(tev[i + 1], main.cuda_stream)
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t_start
+    sclk1 = gpu_sclk_mhz()
+    per_step = sorted(events.elapsed_ms(tev[i], tev[i + 1]) for i in range(steps))
+    events.destroy(tev)
+    spread = {"median_ms": round(per_step[len(per_step) // 2] if steps % 2 else
+                                 0.5 * (per_step[steps // 2 - 1] + per_step[steps // 2]), 4),
+              "min_ms": round(per_step[0], 4), "max_ms": round(per_step[-1], 4),
+              "sclk_mhz_before_after": [sclk0, sclk1]}
     arrays = [ev_arr_t(*evs[i * 2 * len(STAGES):(i + 1) * 2 * len(STAGES)]) for i in range(steps)]
     for i in range(steps):
         step(arrays[i])
@@ -215,7 +248,7 @@ def run_workload(name, steps, warmup, events: HipEvents, extra=False, one_stream
     avg = {s: (sum(v) / len(v) if v else 0.0) for s, v in stage_ms.items()}
     counts_np = counts.cpu().numpy()
     res = dict(cfg=cfg, elapsed=elapsed, ms_per_step=elapsed / steps * 1e3, stage_ms=avg,
-               counts=counts_np, inputs=inp)
+               counts=counts_np, inputs=inp, step_spread=spread)
     if extra:
         res["next_rows"] = time_next_rows(moe, c, dev, counts, events, main)
     del dev, out
@@ -239,6 +272,7 @@ def fp8_prefill_summary(r):
             "ms_per_step": round(r["ms_per_step"], 4),
             "tokens_per_s": round(cfg.T / (r["ms_per_step"] * 1e-3), 1),
             "up_ms": round(up_ms, 4), "down_ms": round(r["stage_ms"]["down"], 4),
+            "step_spread": r["step_spread"],
             "up_tflops": round(flops / (up_ms * 1e-3) / 1e12, 1),
             "up_frac_bf16_peak": round(flops / (up_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)}
 
@@ -271,7 +305,8 @@ def decode_summary(r):
         "workload": cfg.name, "T": cfg.T, "ms_per_step": round(ms, 4),
         "hbm_GBps": round(gbps, 1), "hbm_frac": round(gbps / PEAK_HBM_GBPS, 4),
         "n_active_routed": n_active, "idle_experts": int(cfg.n_routed - n_active),
-        "weight_bytes_per_step": total_bytes, "stage_ms": {k: round(v, 4) for k, v in r["stage_ms"].items()},
+        "weight_bytes_per_step": total_bytes, "step_spread": r["step_spread"],
+        "stage_ms": {k: round(v, 4) for k, v in r["stage_ms"].items()},
         "roofline": {"bound": "hbm", "kernel": "gemm_fp8_small_kernel<SwiGLU> (routed W1|W3 fp8)",
                      "achieved": round(up_gbps, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
                      "frac": round(up_gbps / PEAK_HBM_GBPS, 4), "algorithmic_per_launch": up_bytes,
@@ -511,6 +546,7 @@ def main():
                    "n_shared": cfg.n_shared, "inter": cfg.inter, "k": cfg.k,
                    "groups": f"{cfg.topk_groups}/{cfg.n_groups}", "gate": cfg.gate},
         "layer_mfma_frac": round(flops / (r["ms_per_step"] * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+        "step_spread": r["step_spread"],
         "stage_ms": {k: round(v, 4) for k, v in r["stage_ms"].items()},
         "roofline": prefill_roofline(r),
         "next_rows": r.get("next_rows"),
