@@ -198,11 +198,16 @@ def run_workload(name, steps, warmup, events: HipEvents, extra=False, one_stream
         torch.cuda.synchronize()
         run = g.replay
     # Sustained-load warm-up before the timed steps: at least `warmup` more
-    # forwards and at least WARM_S seconds of back-to-back ones.  A kernel trace
-    # of replayed decode forwards after the idle gap of graph capture shows
-    # forwards slowing from 1.20 to 1.46 ms and settling at 1.13-1.15 ms after
-    # about 15 of them (clocks adjusting to the load), which a fixed count of
-    # a few steps does not cover.
+    # forwards and at least WARM_S seconds of back-to-back ones, and no idle
+    # gap between it and the timed steps.  After an idle gap (graph capture,
+    # a host call of a few hundred ms) replayed decode forwards slow from 1.20
+    # to 1.41 ms and settle at 1.13 ms only after about 15 of them, prefill
+    # forwards take 16.8 and 15.1 ms before settling at 14.5 ms (clocks
+    # adjusting to the load); a fixed count of a few steps does not cover it.
+    sclk0 = gpu_sclk_mhz()  # before the warm-up: an idle gap after it slows the next steps
+    tev = events.create(steps + 1)
+    rec = events.hip.hipEventRecord
+    rec.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
     t_w = time.perf_counter()
     n_w = 0
     while n_w < warmup or time.perf_counter() - t_w < WARM_S:
@@ -211,14 +216,10 @@ def run_workload(name, steps, warmup, events: HipEvents, extra=False, one_stream
         if n_w % 8 == 0:
             torch.cuda.synchronize()  # keep the host's clock on the GPU's
     torch.cuda.synchronize()
-    # the timed steps carry no stage events; the per-stage times come from as
-    # many eager steps again, each stage bracketed by events on its own stream
-    # one event after each timed step on the stream the steps run on: the
-    # per-step median and spread (the host clock gives the total)
-    tev = events.create(steps + 1)
-    rec = events.hip.hipEventRecord
-    rec.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
-    sclk0 = gpu_sclk_mhz()
+    # the timed steps carry no stage events (the per-stage times come from as
+    # many eager steps again, each stage bracketed by events on its own
+    # stream), only one event after each step on the stream the steps run on,
+    # for the per-step median and spread (the host clock gives the total)
     t_start = time.perf_counter()
     rec(tev[0], main.cuda_stream)
     for i in range(steps):
@@ -227,12 +228,13 @@ def run_workload(name, steps, warmup, events: HipEvents, extra=False, one_stream
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t_start
     sclk1 = gpu_sclk_mhz()
-    per_step = sorted(events.elapsed_ms(tev[i], tev[i + 1]) for i in range(steps))
+    in_order = [events.elapsed_ms(tev[i], tev[i + 1]) for i in range(steps)]
+    per_step = sorted(in_order)
     events.destroy(tev)
     spread = {"median_ms": round(per_step[len(per_step) // 2] if steps % 2 else
                                  0.5 * (per_step[steps // 2 - 1] + per_step[steps // 2]), 4),
               "min_ms": round(per_step[0], 4), "max_ms": round(per_step[-1], 4),
-              "sclk_mhz_before_after": [sclk0, sclk1]}
+              "sclk_mhz": {"before_warmup": sclk0, "after_timed": sclk1}}
     arrays = [ev_arr_t(*evs[i * 2 * len(STAGES):(i + 1) * 2 * len(STAGES)]) for i in range(steps)]
     for i in range(steps):
         step(arrays[i])
@@ -248,7 +250,7 @@ def run_workload(name, steps, warmup, events: HipEvents, extra=False, one_stream
     avg = {s: (sum(v) / len(v) if v else 0.0) for s, v in stage_ms.items()}
     counts_np = counts.cpu().numpy()
     res = dict(cfg=cfg, elapsed=elapsed, ms_per_step=elapsed / steps * 1e3, stage_ms=avg,
-               counts=counts_np, inputs=inp, step_spread=spread)
+               counts=counts_np, inputs=inp, step_spread=spread, step_ms=in_order)
     if extra:
         res["next_rows"] = time_next_rows(moe, c, dev, counts, events, main)
     del dev, out
