@@ -268,6 +268,42 @@ __device__ __forceinline__ int unpack_idx(uint64_t p) {
   return (int)(0xffffffffu - (uint32_t)(p & 0xffffffffu));
 }
 
+// Group scores when a group is 2^STEPS consecutive experts (2..64): group
+// j * (64 >> STEPS) + lane >> STEPS is a segment of lanes of register j, so
+// all groups find their top entries at once with segmented maxima.  Each
+// group's score adds its group_topn largest keys, largest first, from 0.
+// Returns, in lane g < n_groups, the score of group g.
+template <int STEPS>
+__device__ __forceinline__ float group_scores_segmented(const float (&key)[kSelPerLane],
+                                                        const bool (&ok)[kSelPerLane], int lane,
+                                                        int n_groups, int group_topn) {
+  constexpr int GS = 1 << STEPS, SEG = 64 / GS;  // lanes per group, groups per register
+  float s[kSelPerLane];
+  unsigned taken = 0;
+#pragma unroll
+  for (int j = 0; j < kSelPerLane; ++j) s[j] = 0.f;
+  for (int r = 0; r < group_topn; ++r) {
+    uint64_t best[kSelPerLane];
+#pragma unroll
+    for (int j = 0; j < kSelPerLane; ++j)
+      best[j] = ok[j] && !((taken >> j) & 1u) ? pack_key(key[j], lane + 64 * j) : 0;
+#pragma unroll
+    for (int j = 0; j < kSelPerLane; ++j) best[j] = segment_max_u64<STEPS>(best[j]);
+#pragma unroll
+    for (int j = 0; j < kSelPerLane; ++j) {
+      if (best[j] != 0 && (unpack_idx(best[j]) & 63) == lane) taken |= 1u << j;
+      s[j] += ordered_to_f32((uint32_t)(best[j] >> 32));
+    }
+  }
+  float mine = -__builtin_inff();
+#pragma unroll
+  for (int j = 0; j < kSelPerLane; ++j) {
+    const float v = __shfl(s[j], (lane % SEG) * GS, 64);
+    if (lane < n_groups && lane / SEG == j) mine = v;
+  }
+  return mine;
+}
+
 // R > 0 (N % 4 == 0): lane l adds the partials of experts 4l .. 4l+3 with
 // 16-byte loads, R splits in flight at a time, and the sums go through LDS to
 // the lanes that select.  R == 0: one expert per load, 8 splits at a time.
@@ -279,7 +315,7 @@ __global__ __launch_bounds__(256) void router_select_kernel(
     int32_t* __restrict__ out_idx, float* __restrict__ out_gate, float* __restrict__ scores) {
   const int lane = lane_id();
   const int wv = threadIdx.x >> 6;
-  const int64_t t = (int64_t)blockIdx.x * 4 + wv;
+  const int64_t t = (int64_t)blockIdx.x * (blockDim.x >> 6) + wv;
   if (t >= T) return;  // uniform per wavefront
   const float NEG_INF = -__builtin_inff();
 
@@ -407,26 +443,37 @@ __global__ __launch_bounds__(256) void router_select_kernel(
   // ---- group limit: score = sum of the group_topn largest keys of the group
   if (n_groups > 1) {
     const int gs = N / n_groups;
-    float my_gscore = NEG_INF;
-    for (int g = 0; g < n_groups; ++g) {
-      unsigned taken = 0;
-      float s = 0.f;
-      for (int r = 0; r < group_topn; ++r) {
-        uint64_t best = 0;
+    int grp[kSelPerLane];
 #pragma unroll
-        for (int j = 0; j < kSelPerLane; ++j) {
-          const int e = lane + 64 * j;
-          if (ok[j] && e / gs == g && !((taken >> j) & 1u)) {
-            const uint64_t p = pack_key(key[j], e);
-            best = p > best ? p : best;
+    for (int j = 0; j < kSelPerLane; ++j) grp[j] = (lane + 64 * j) / gs;
+    float my_gscore = NEG_INF;
+    switch (gs) {
+      case 2: my_gscore = group_scores_segmented<1>(key, ok, lane, n_groups, group_topn); break;
+      case 4: my_gscore = group_scores_segmented<2>(key, ok, lane, n_groups, group_topn); break;
+      case 8: my_gscore = group_scores_segmented<3>(key, ok, lane, n_groups, group_topn); break;
+      case 16: my_gscore = group_scores_segmented<4>(key, ok, lane, n_groups, group_topn); break;
+      case 32: my_gscore = group_scores_segmented<5>(key, ok, lane, n_groups, group_topn); break;
+      case 64: my_gscore = group_scores_segmented<6>(key, ok, lane, n_groups, group_topn); break;
+      default:  // one group at a time over the whole wavefront
+        for (int g = 0; g < n_groups; ++g) {
+          unsigned taken = 0;
+          float s = 0.f;
+          for (int r = 0; r < group_topn; ++r) {
+            uint64_t best = 0;
+#pragma unroll
+            for (int j = 0; j < kSelPerLane; ++j) {
+              if (ok[j] && grp[j] == g && !((taken >> j) & 1u)) {
+                const uint64_t p = pack_key(key[j], lane + 64 * j);
+                best = p > best ? p : best;
+              }
+            }
+            best = wave_max_u64(best);
+            const int e_sel = unpack_idx(best);
+            if ((e_sel & 63) == lane) taken |= 1u << (e_sel >> 6);
+            s += ordered_to_f32((uint32_t)(best >> 32));
           }
+          if (lane == g) my_gscore = s;
         }
-        best = wave_max_u64(best);
-        const int e_sel = unpack_idx(best);
-        if ((e_sel & 63) == lane) taken |= 1u << (e_sel >> 6);
-        s += ordered_to_f32((uint32_t)(best >> 32));
-      }
-      if (lane == g) my_gscore = s;
     }
     uint64_t allowed = 0;
     for (int r = 0; r < topk_groups; ++r) {
@@ -436,10 +483,8 @@ __global__ __launch_bounds__(256) void router_select_kernel(
       allowed |= 1ull << unpack_idx(p);
     }
 #pragma unroll
-    for (int j = 0; j < kSelPerLane; ++j) {
-      const int e = lane + 64 * j;
-      if (ok[j] && !((allowed >> (e / gs)) & 1ull)) key[j] = NEG_INF;
-    }
+    for (int j = 0; j < kSelPerLane; ++j)
+      if (ok[j] && !((allowed >> grp[j]) & 1ull)) key[j] = NEG_INF;
   }
 
   // ---- top-k (k <= 64): lane i keeps the i-th selection
@@ -484,11 +529,14 @@ hipError_t launch_router_select(const float* z, int nsplit, const float* b, int6
                                 int n_groups, int topk_groups, int group_topn, int gate,
                                 float route_scale, int32_t* idx, float* gates, float* scores,
                                 hipStream_t stream, const ExpertMask* mask) {
-  const unsigned blocks = (unsigned)cdiv(T, 4);
+  // one wavefront per token; a few tokens (decode) get a block each, so that
+  // their loads of the partials spread over as many CUs
+  const int wpb = T < 1024 ? 1 : 4;
+  const unsigned blocks = (unsigned)cdiv(T, wpb);
   const ExpertMask m = mask ? *mask : ExpertMask{};
   const bool vec = N % 4 == 0 && ((uintptr_t)z & 15) == 0;
 #define MOE_SELECT(R)                                                                          \
-  router_select_kernel<R><<<blocks, 256, 0, stream>>>(z, nsplit, b, T, N, k, n_groups,         \
+  router_select_kernel<R><<<blocks, 64 * wpb, 0, stream>>>(z, nsplit, b, T, N, k, n_groups,    \
                                                       topk_groups, group_topn, gate,           \
                                                       route_scale, m, idx, gates, scores)
   if (!vec) MOE_SELECT(0);

@@ -73,6 +73,21 @@ struct MaxU64Step {
   }
 };
 
+// Max over aligned segments of 2^STEPS lanes, in every lane of the segment:
+// the first STEPS steps of the wavefront reduction above.
+template <int STEPS>
+__device__ __forceinline__ uint64_t segment_max_u64(uint64_t v) {
+  static_assert(STEPS >= 1 && STEPS <= 6, "segments of 2 to 64 lanes");
+  const MaxU64Step st;
+  v = st.template dpp<kDppXor1>(v);
+  if (STEPS > 1) v = st.template dpp<kDppXor2>(v);
+  if (STEPS > 2) v = st.template dpp<kDppHalfMirror>(v);
+  if (STEPS > 3) v = st.template dpp<kDppRowMirror>(v);
+  if (STEPS > 4) v = st.swap16(v);
+  if (STEPS > 5) v = st.swap32(v);
+  return v;
+}
+
 __device__ __forceinline__ float wave_max(float v) { return wave_reduce_exact(v, MaxF32Step{}); }
 __device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
   return wave_reduce_exact(v, MaxU64Step{});

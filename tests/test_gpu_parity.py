@@ -104,6 +104,28 @@ def test_router_masked(lib, name, mask_top, drop_every):
     assert s_err < 2e-5
 
 
+# group sizes 2..64 take the segmented group scores, 12 and 128 the one-group-
+# at-a-time path; the router keeps the V3 form (sigmoid, bias, top-2 group score)
+@pytest.mark.parametrize("N,G,TG,k", [(16, 8, 3, 4), (32, 8, 4, 6), (64, 8, 4, 8), (64, 4, 2, 5),
+                                      (128, 4, 2, 8), (256, 4, 3, 8), (96, 8, 4, 6),
+                                      (256, 2, 1, 8)])
+def test_router_group_sizes(lib, N, G, TG, k):
+    cfg = datagen.get_config("v3_prefill", T=1500, d=512, inter=128, n_routed=N, n_groups=G,
+                             topk_groups=TG, k=k)
+    say(f"[router-groups] N={N} groups={G} (size {N // G}) top-groups={TG} k={k}")
+    inp = datagen.MoEInputs(cfg)
+    x = inp.x()
+    r = oracle_route(cfg, inp, x)
+    c = lib.config_from(cfg)
+    dev = torch.device("cuda")
+    idx, gate, scores = lib.router(c, to_torch(x, dev), to_torch(inp.router_w(), dev),
+                                   to_torch(inp.router_b(), dev), want_scores=True)
+    torch.cuda.synchronize()
+    near, order = check_routing(cfg, r, idx.cpu().numpy(), gate.cpu().numpy())
+    say(f"   near-ties {near}/{cfg.T}, order diffs {order}")
+    assert near < cfg.T // 50
+
+
 def test_bias_update_bit_exact(lib):
     """The aux-loss-free step on the GPU equals the oracle's bit for bit, over
     loads below, at and above the mean, applied repeatedly."""
