@@ -111,9 +111,14 @@ def time_next_rows(moe, c, dev, counts, events: HipEvents, stream, reps=20):
     }
     out = {}
     for name, fn in calls.items():
-        fn()
-        torch.cuda.synchronize()
         e0, e1 = events.create(2)
+        t_w = time.perf_counter()
+        n_w = 0
+        while time.perf_counter() - t_w < 0.1:  # back-to-back calls first (clocks)
+            fn()
+            n_w += 1
+            if n_w % 16 == 0:
+                torch.cuda.synchronize()
         rec = events.hip.hipEventRecord
         rec.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
         rec(e0, stream.cuda_stream)
@@ -127,24 +132,24 @@ def time_next_rows(moe, c, dev, counts, events: HipEvents, stream, reps=20):
 
 
 WARM_S = 0.5  # seconds of back-to-back forwards before the timed ones
+RESTAGE_S = 0.25  # seconds of eager forwards before the stage-event ones
 
 
 def gpu_sclk_mhz():
-    """The GPU's current shader clock in MHz as rocm-smi reports it, or None."""
-    import shutil
-    import subprocess
-    exe = shutil.which("rocm-smi") or "/opt/rocm/bin/rocm-smi"
-    try:
-        r = subprocess.run([exe, "--showclocks", "--json"], capture_output=True, text=True,
-                           timeout=20)
-        d = json.loads(r.stdout)
-        for card in d.values():
-            for k, v in card.items():
-                if "sclk" in k.lower() and "speed" in k.lower():
-                    return int(float(str(v).strip("()Mhz ").split()[0]))
-    except Exception:
-        return None
-    return None
+    """The GPU's current shader clock in MHz: the level marked current in the
+    driver's sysfs table (the file rocm-smi reads), or None if there is not
+    exactly one such GPU.  A plain file read: no child process."""
+    import glob
+    found = []
+    for path in glob.glob("/sys/class/drm/card*/device/pp_dpm_sclk"):
+        try:
+            with open(path) as f:
+                for line in f:
+                    if line.rstrip().endswith("*"):
+                        found.append(int(line.split(":")[1].strip().lower().split("mhz")[0]))
+        except (OSError, ValueError, IndexError):
+            continue
+    return found[0] if len(found) == 1 else None
 
 
 def run_workload(name, steps, warmup, events: HipEvents, extra=False, one_stream=False,
@@ -227,6 +232,19 @@ def run_workload(name, steps, warmup, events: HipEvents, extra=False, one_stream
         rec(tev[i + 1], main.cuda_stream)
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t_start
+    # the stage-event steps follow at once, after RESTAGE_S more seconds of
+    # eager forwards, so that they too run at the clocks of sustained load
+    arrays = [ev_arr_t(*evs[i * 2 * len(STAGES):(i + 1) * 2 * len(STAGES)]) for i in range(steps)]
+    t_w = time.perf_counter()
+    n_w = 0
+    while time.perf_counter() - t_w < RESTAGE_S:
+        step(None)
+        n_w += 1
+        if n_w % 8 == 0:
+            torch.cuda.synchronize()
+    for i in range(steps):
+        step(arrays[i])
+    torch.cuda.synchronize()
     sclk1 = gpu_sclk_mhz()
     in_order = [events.elapsed_ms(tev[i], tev[i + 1]) for i in range(steps)]
     per_step = sorted(in_order)
@@ -234,11 +252,7 @@ def run_workload(name, steps, warmup, events: HipEvents, extra=False, one_stream
     spread = {"median_ms": round(per_step[len(per_step) // 2] if steps % 2 else
                                  0.5 * (per_step[steps // 2 - 1] + per_step[steps // 2]), 4),
               "min_ms": round(per_step[0], 4), "max_ms": round(per_step[-1], 4),
-              "sclk_mhz": {"before_warmup": sclk0, "after_timed": sclk1}}
-    arrays = [ev_arr_t(*evs[i * 2 * len(STAGES):(i + 1) * 2 * len(STAGES)]) for i in range(steps)]
-    for i in range(steps):
-        step(arrays[i])
-    torch.cuda.synchronize()
+              "sclk_mhz": {"before_warmup": sclk0, "after_stage_steps": sclk1}}
     stage_ms = {s: [] for s in STAGES}
     for i in range(steps):
         base = i * 2 * len(STAGES)
@@ -497,9 +511,69 @@ def summarize_util(csv_path, command, out_path):
     print(text)
 
 
+STALL_A = ("GRBM_GUI_ACTIVE SQ_WAVE_CYCLES SQ_WAIT_ANY SQ_WAIT_INST_ANY SQ_ACTIVE_INST_ANY "
+           "SQ_ACTIVE_INST_LDS SQ_ACTIVE_INST_VALU SQ_ACTIVE_INST_VMEM SQ_VALU_MFMA_BUSY_CYCLES")
+STALL_B = ("GRBM_GUI_ACTIVE SQ_WAIT_INST_LDS SQ_LDS_DATA_FIFO_FULL SQ_LDS_CMD_FIFO_FULL "
+           "SQ_VMEM_TA_ADDR_FIFO_FULL SQ_VMEM_TA_CMD_FIFO_FULL SQ_ACTIVE_INST_SCA SQ_ACTIVE_INST_MISC "
+           "SQ_VALU_MFMA_COEXEC_CYCLES")
+
+
+def summarize_stalls(csv_a, csv_b, command, out_path):
+    """Where the wavefronts of the routed bf16 GEMMs spend their cycles, from two
+    rocprofv3 --pmc passes (STALL_A, STALL_B) of the same command: every count
+    as a fraction of the SIMD-cycles of the launch (GRBM_GUI_ACTIVE / 8 XCDs x
+    1024 SIMDs; one wavefront per SIMD).  SQ_WAVE_CYCLES and the SQ_WAIT_*
+    counters count in units of 4 cycles."""
+    import collections
+    import csv
+    quad = {"SQ_WAVE_CYCLES", "SQ_WAIT_ANY", "SQ_WAIT_INST_ANY", "SQ_WAIT_INST_LDS"}
+    targets = {"bf16 routed up": "gemm_bf16_persist_kernel<32, 4, true, false>",
+               "bf16 routed down": "gemm_bf16_persist_kernel<32, 4, false, false>"}
+    res = collections.defaultdict(dict)
+    for path in (csv_a, csv_b):
+        per = collections.defaultdict(lambda: collections.defaultdict(float))
+        names = {}
+        for r in csv.DictReader(open(path)):
+            key = (r["Kernel_Name"], int(r["Dispatch_Id"]))
+            per[key][r["Counter_Name"]] += float(r["Counter_Value"])
+            names[key] = r["Kernel_Name"]
+        for label, pat in targets.items():
+            keys = [k for k in per if pat in names[k]]
+            if not keys:
+                continue
+            gmax = max(per[k]["GRBM_GUI_ACTIVE"] for k in keys)
+            keys = [k for k in keys if per[k]["GRBM_GUI_ACTIVE"] >= 0.5 * gmax]  # routed launches
+            n = len(keys)
+            simd_cycles = sum(per[k]["GRBM_GUI_ACTIVE"] for k in keys) / n / 8 * 1024
+            for c in per[keys[0]]:
+                if c == "GRBM_GUI_ACTIVE":
+                    continue
+                v = sum(per[k][c] for k in keys) / n * (4 if c in quad else 1)
+                res[label][c] = (v / simd_cycles, n)
+    lines = ["# Stall breakdown of the routed bf16 GEMM launches (rocprofv3 --pmc, two passes)",
+             "# command of each pass (run from /tmp, TMPDIR=/tmp), counters STALL_A then STALL_B of bench.py:",
+             f"#   {command}",
+             "# summary: python bench.py --summarize-stalls <passA>/bench_counter_collection.csv "
+             "<passB>/bench_counter_collection.csv '<command>' <this file>",
+             "# fraction of the launch's SIMD-cycles (GRBM_GUI_ACTIVE / 8 XCDs x 1024 SIMDs), averaged over",
+             "# the routed launches (at least half the longest); SQ_WAVE_CYCLES and SQ_WAIT_* count 4 cycles each",
+             f"{'counter':30s} " + " ".join(f"{lab:>18s}" for lab in targets)]
+    counters = sorted({c for lab in res for c in res[lab]})
+    for c in counters:
+        row = " ".join(f"{res[lab][c][0]:18.3f}" if c in res[lab] else f"{'-':>18s}" for lab in targets)
+        lines.append(f"{c:30s} {row}")
+    text = "\n".join(lines) + "\n"
+    with open(out_path, "w") as f:
+        f.write(text)
+    print(text)
+
+
 def main():
     if len(sys.argv) > 1 and sys.argv[1] == "--summarize-util":
         summarize_util(sys.argv[2], sys.argv[3], sys.argv[4])
+        return
+    if len(sys.argv) > 1 and sys.argv[1] == "--summarize-stalls":
+        summarize_stalls(sys.argv[2], sys.argv[3], sys.argv[4], sys.argv[5])
         return
     if len(sys.argv) > 1 and sys.argv[1] == "--summarize-trace":
         summarize_trace(sys.argv[2], sys.argv[3] if len(sys.argv) > 3 else "")
