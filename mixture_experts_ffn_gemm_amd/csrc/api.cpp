@@ -31,8 +31,9 @@ size_t align_up(size_t v) { return (v + 255) & ~size_t(255); }
 
 struct Layout {
   size_t z, idx, gate, hist, base, rank, counts, offsets, row_token, slot_row, h, y, hs, ys,
-      shoff, total;
-  int64_t h_elems;  // capacity of the h region in activation elements
+      shoff, zrow[2], total;
+  int64_t h_elems;     // capacity of the h region in activation elements
+  int64_t zrow_elems;  // capacity of each zero region in bf16 elements
 };
 
 // bf16 or fp8 with one shared expert and no second stream to overlap it on:
@@ -75,6 +76,11 @@ Layout make_layout(const moe_config& c) {
   L.hs = take(T * S * I * as);
   L.ys = take(S > 0 ? T * d * as : 0);
   L.shoff = take(2 * 4);
+  // two regions of kZeroRows zero rows (routed GEMMs; shared expert on the
+  // side stream), each row as long as the longest K of the persistent GEMMs
+  L.zrow_elems = (int64_t)align_up((size_t)kZeroRows * (d > inter_max ? d : inter_max) * 2) / 2;
+  L.zrow[0] = take(L.zrow_elems * 2);
+  L.zrow[1] = take(L.zrow_elems * 2);
   L.total = off;
   return L;
 }
@@ -189,7 +195,8 @@ int run_expert_ffn(const moe_config* c, int n_experts, const int32_t* offsets, i
                    void* const* ev = nullptr, int stage_up = -1, int stage_dn = -1,
                    const void* W1x = nullptr, const void* W3x = nullptr,
                    const void* W2x = nullptr, const float* s1x = nullptr,
-                   const float* s3x = nullptr, const float* s2x = nullptr) {
+                   const float* s3x = nullptr, const float* s2x = nullptr,
+                   void* zrow = nullptr, int64_t zrow_elems = 0, hipEvent_t after_up = nullptr) {
   GroupedGemmArgs up{};
   up.B0x = W1x;
   up.B1x = W3x;
@@ -223,22 +230,34 @@ int run_expert_ffn(const moe_config* c, int n_experts, const int32_t* offsets, i
   dn.Nout = c->d;
   dn.K = inter;
   // bf16: the persistent kernel takes K >= 128 (four 32-deep steps) and
-  // A byte offsets below 4 GiB; anything else goes to the 8-wave kernel
-  auto bf16_gemm = [&](const GroupedGemmArgs& a, bool swiglu, int64_t a_rows) {
-    if (a.K % 32 == 0 && a.K >= 128 && a_rows * (int64_t)a.K * 2 < (int64_t(1) << 32) - 4096)
-      return launch_gemm_bf16_persist(a, swiglu, s);
-    return launch_gemm_bf16_v2(a, swiglu, s);
-  };
+  // A byte offsets below 4 GiB; anything else goes to the 8-wave kernel.
   // fp8: many rows per expert (prefill) take the persistent MFMA kernel with
   // the weights dequantized to bf16 in registers; a few rows per expert
-  // (decode) the weight-streaming kernel
-  auto fp8_gemm = [&](const GroupedGemmArgs& a, bool swiglu, int64_t a_rows) {
-    if (a.max_rows >= 128 * (int64_t)a.n_groups && a.K >= 128 &&
-        a_rows * (int64_t)a.K * 2 < (int64_t(1) << 32) - 4096)
-      return launch_gemm_fp8_persist(a, swiglu, s);
-    return swiglu ? launch_gemm_fp8_swiglu(a, s) : launch_gemm_fp8_store(a, s);
+  // (decode) the weight-streaming kernel.
+  auto persistent = [&](const GroupedGemmArgs& a, int64_t a_rows) {
+    const bool fits = a.K % 32 == 0 && a.K >= 128 &&
+                      a_rows * (int64_t)a.K * 2 < (int64_t(1) << 32) - 4096;
+    if (c->w_dtype == MOE_BF16) return fits;
+    return c->w_dtype == MOE_FP8_E4M3 && fits && a.max_rows >= 128 * (int64_t)a.n_groups;
   };
   const int64_t up_rows = row_index ? (c->T > max_rows ? c->T : max_rows) : max_rows;
+  // the persistent kernels' rows past a tile's last read a row of zeros
+  // (same results, less power than repeating the last row): cleared here
+  const int64_t kmax = c->d > inter ? c->d : inter;
+  if (zrow && zrow_elems >= kZeroRows * kmax &&
+      (persistent(up, up_rows) || persistent(dn, max_rows))) {
+    MOE_HIP_CHECK(launch_fill_i32((int32_t*)zrow, kZeroRows * kmax / 2, 0, s));
+    up.zero_row = zrow;
+    dn.zero_row = zrow;
+  }
+  auto bf16_gemm = [&](const GroupedGemmArgs& a, bool swiglu, int64_t a_rows) {
+    if (persistent(a, a_rows)) return launch_gemm_bf16_persist(a, swiglu, s);
+    return launch_gemm_bf16_v2(a, swiglu, s);
+  };
+  auto fp8_gemm = [&](const GroupedGemmArgs& a, bool swiglu, int64_t a_rows) {
+    if (persistent(a, a_rows)) return launch_gemm_fp8_persist(a, swiglu, s);
+    return swiglu ? launch_gemm_fp8_swiglu(a, s) : launch_gemm_fp8_store(a, s);
+  };
   MOE_HIP_CHECK(mark(ev, stage_up, false, s));
   if (c->w_dtype == MOE_F32)
     MOE_HIP_CHECK(launch_gemm_f32_swiglu(up, s));
@@ -247,6 +266,7 @@ int run_expert_ffn(const moe_config* c, int n_experts, const int32_t* offsets, i
   else
     MOE_HIP_CHECK(fp8_gemm(up, true, up_rows));
   MOE_HIP_CHECK(mark(ev, stage_up, true, s));
+  if (after_up) MOE_HIP_CHECK(hipEventRecord(after_up, s));
   MOE_HIP_CHECK(mark(ev, stage_dn, false, s));
   if (c->w_dtype == MOE_F32)
     MOE_HIP_CHECK(launch_gemm_f32_store(dn, s));
@@ -376,7 +396,9 @@ int moe_expert_ffn(const moe_config* cfg, int32_t n_experts, const int32_t* offs
     return fail(MOE_ERR_WORKSPACE, "max_rows * inter exceeds the workspace sized for this config");
   if (max_rows > 0x7fffffffLL) return fail(MOE_ERR_UNSUPPORTED, "max_rows must fit int32");
   return run_expert_ffn(cfg, n_experts, offsets, max_rows, inter, x_rows, row_index, W1, W3, W2,
-                        s1, s3, s2, at<void>(ws, L.h), y_rows, (hipStream_t)stream);
+                        s1, s3, s2, at<void>(ws, L.h), y_rows, (hipStream_t)stream, nullptr, -1, -1,
+                        nullptr, nullptr, nullptr, nullptr, nullptr, nullptr,
+                        at<void>(ws, L.zrow[0]), L.zrow_elems);
 }
 
 int moe_combine(const moe_config* cfg, const void* y_perm, const int32_t* slot_row,
@@ -434,25 +456,38 @@ static int forward_impl(const moe_config* cfg, const void* x, const float* W_r, 
   } evs;
   hipEvent_t& ev_fork = evs.fork;
   hipEvent_t& ev_join = evs.join;
+  // Where the shared expert starts on the side stream.  Few rows per routed
+  // expert (decode): with the router, whose phase leaves HBM idle, the
+  // layer being bound by streaming weights.  Many (prefill): when the routed
+  // up projection has ended, overlapping the routed down projection; the
+  // routed up GEMM then runs alone, and the forward takes as long as when the
+  // shared expert starts with the router.
+  const bool fork_early = c.T * (int64_t)c.k < 128 * (int64_t)c.n_routed;
   if (two_streams) {
     MOE_HIP_CHECK(hipEventCreateWithFlags(&ev_fork, hipEventDisableTiming));
     MOE_HIP_CHECK(hipEventCreateWithFlags(&ev_join, hipEventDisableTiming));
-    MOE_HIP_CHECK(hipEventRecord(ev_fork, sm));
-    MOE_HIP_CHECK(hipStreamWaitEvent(ss, ev_fork, 0));
   }
   void* ys = nullptr;
-  if (c.n_shared > 0 && !fold) {
-    // shared MLP of width S * I over every token (one expert, rows {0, T})
+  // shared MLP of width S * I over every token (one expert, rows {0, T})
+  auto run_shared = [&]() -> int {
+    if (two_streams) MOE_HIP_CHECK(hipStreamWaitEvent(ss, ev_fork, 0));
     int32_t* shoff = at<int32_t>(ws, L.shoff);
     ys = at<void>(ws, L.ys);
     MOE_HIP_CHECK(launch_set_range(shoff, (int32_t)c.T, ss));
-    st = run_expert_ffn(cfg, 1, shoff, c.T, c.n_shared * c.inter, x, nullptr, W1s, W3s, W2s, s1s,
-                        s3s, s2s, at<void>(ws, L.hs), ys, ss, ev, MOE_STAGE_SHARED_UP,
-                        MOE_STAGE_SHARED_DOWN);
-    if (st) return st;
+    const int r = run_expert_ffn(cfg, 1, shoff, c.T, c.n_shared * c.inter, x, nullptr, W1s, W3s,
+                                 W2s, s1s, s3s, s2s, at<void>(ws, L.hs), ys, ss, ev,
+                                 MOE_STAGE_SHARED_UP, MOE_STAGE_SHARED_DOWN, nullptr, nullptr,
+                                 nullptr, nullptr, nullptr, nullptr, at<void>(ws, L.zrow[1]),
+                                 L.zrow_elems);
+    if (r) return r;
     if (two_streams) MOE_HIP_CHECK(hipEventRecord(ev_join, ss));
+    return MOE_OK;
+  };
+  const bool shared_side = c.n_shared > 0 && !fold;
+  if (shared_side && fork_early) {
+    if (two_streams) MOE_HIP_CHECK(hipEventRecord(ev_fork, sm));
+    if ((st = run_shared())) return st;
   }
-
   int32_t* idx = topk_idx_out ? topk_idx_out : at<int32_t>(ws, L.idx);
   float* gate = topk_gate_out ? topk_gate_out : at<float>(ws, L.gate);
   int32_t* counts = counts_out ? counts_out : at<int32_t>(ws, L.counts);
@@ -476,7 +511,8 @@ static int forward_impl(const moe_config* cfg, const void* x, const float* W_r, 
     // routed experts and the shared expert (group n_routed) in one launch each
     st = run_expert_ffn(cfg, c.n_routed + 1, offsets, slots + c.T, c.inter, x, row_token, W1, W3,
                         W2, s1, s3, s2, at<void>(ws, L.h), y, sm, ev, MOE_STAGE_UP,
-                        MOE_STAGE_DOWN, W1s, W3s, W2s, s1s, s3s, s2s);
+                        MOE_STAGE_DOWN, W1s, W3s, W2s, s1s, s3s, s2s, at<void>(ws, L.zrow[0]),
+                        L.zrow_elems);
     ys = (char*)y + slots * c.d * act_bytes(c.act_dtype);
     for (int stg : {MOE_STAGE_SHARED_UP, MOE_STAGE_SHARED_DOWN}) {  // folded: empty intervals
       MOE_HIP_CHECK(mark(ev, stg, false, sm));
@@ -484,9 +520,12 @@ static int forward_impl(const moe_config* cfg, const void* x, const float* W_r, 
     }
   } else {
     st = run_expert_ffn(cfg, c.n_routed, offsets, slots, c.inter, x, row_token, W1, W3, W2, s1,
-                        s3, s2, at<void>(ws, L.h), y, sm, ev, MOE_STAGE_UP, MOE_STAGE_DOWN);
+                        s3, s2, at<void>(ws, L.h), y, sm, ev, MOE_STAGE_UP, MOE_STAGE_DOWN, nullptr,
+                        nullptr, nullptr, nullptr, nullptr, nullptr, at<void>(ws, L.zrow[0]),
+                        L.zrow_elems, two_streams && !fork_early ? ev_fork : nullptr);
   }
   if (st) return st;
+  if (shared_side && !fork_early && (st = run_shared())) return st;
   if (two_streams) MOE_HIP_CHECK(hipStreamWaitEvent(sm, ev_join, 0));
   MOE_HIP_CHECK(mark(ev, MOE_STAGE_COMBINE, false, sm));
   MOE_HIP_CHECK(launch_combine(c.act_dtype == MOE_BF16, c.out_dtype == MOE_BF16, y, slot_row, gate,

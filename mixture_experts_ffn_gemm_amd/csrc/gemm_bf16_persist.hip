@@ -25,12 +25,17 @@
 // stores 16 bytes.
 //
 // Every tile does all of its MFMAs, also past an expert's last row (those
-// rows repeat the last row and are not stored): tiles of equal cost keep the
-// workgroups of an XCD in step, so the panels they share are still in L2 when
-// each of them reads them.  Skipping the MFMAs of a partly filled tile made
-// such tiles finish early, the workgroups drifted apart and the routed up
-// projection of the V3-shaped layer read 37 GB past L2 instead of 21 GB and
-// ran 10% slower.
+// rows are not stored): tiles of equal cost keep the workgroups of an XCD in
+// step, so the panels they share are still in L2 when each of them reads
+// them.  Skipping the MFMAs of a partly filled tile made such tiles finish
+// early, the workgroups drifted apart and the routed up projection of the
+// V3-shaped layer read 37 GB past L2 instead of 21 GB and ran 10-19% slower.
+// The rows past the end read rows of zeros when the caller provides them
+// (zero_row: kZeroRows rows of K), else repeat the last row: the chip runs
+// these GEMMs at a clock set by power, and MFMAs on zero operands draw less
+// of it (with all activations zero the routed up projection runs 18% faster).
+// Row r of a tile reads zero row r % kZeroRows, so that the padding loads of
+// all workgroups spread over the L2 channels instead of meeting on one line.
 //
 // Pipeline.  K is staged BK at a time through NS LDS stages by direct
 // global->LDS loads (global_load_lds_dwordx4).  A "step" is one BK slice of one
@@ -219,11 +224,13 @@ __device__ __forceinline__ Tile decode_tile(const TileTab& tt, int n_groups, int
 }
 
 // The issue side of the pipeline: which step's slice the next direct loads
-// fetch, and their sources in the current tile: a wave-uniform base per load
-// and a 32-bit per-lane byte offset.
+// fetch, and their sources in the current tile: for activation rows a
+// per-lane address (a row past the tile's last reads the zero row), for
+// weight rows a wave-uniform base and a 32-bit per-lane byte offset.
 template <int BK, bool SWIGLU, bool W8>
 struct Issuer {
   using G = Geo<BK, W8>;
+  const char* arow[G::A_LOADS];
   const char* base[G::LOADS];
   unsigned off[G::LOADS];
   int it, kt;  // tile index within this workgroup's list, step within the tile
@@ -245,8 +252,10 @@ struct Issuer {
           row = t.row0 + r;
           if (row > t.rend - 1) row = t.rend - 1;
         }
-        base[j] = (const char*)a.A;
-        off[j] = (unsigned)(row * rowb) + (unsigned)(G::swz(r, phys) << 4);
+        const bool pad = a.zero_row && t.row0 + r >= t.rend;
+        arow[j] = (pad ? (const char*)a.zero_row + (r % kZeroRows) * rowb
+                       : (const char*)a.A + row * rowb) +
+                  (G::swz(r, phys) << 4);
       } else {
         // first LDS row of the block (0..255), this lane's row in it, and the
         // 16-byte piece of the row's step slice that goes to this lane's slot
@@ -271,8 +280,8 @@ struct Issuer {
 
   // Direct load j of the current step into `stage`.
   __device__ __forceinline__ void load(int j, char* stage, int wv) const {
-    const int step = j < G::A_LOADS ? BK * 2 : G::B_STEP;
-    __builtin_amdgcn_global_load_lds((const void*)(base[j] + kt * step + off[j]),
+    const char* src = j < G::A_LOADS ? arow[j] + kt * (BK * 2) : base[j] + kt * G::B_STEP + off[j];
+    __builtin_amdgcn_global_load_lds((const void*)src,
                                      (lds_void*)(stage + (NWAVE * j + wv) * 1024), 16, 0, 0);
   }
 };
