@@ -212,10 +212,14 @@ int moe_combine(const moe_config* cfg, const void* y_perm, const int32_t* slot_r
 /*
  * moe_forward - the whole layer: router -> permute -> routed experts (fused
  * gather) -> combine.  The shared MLP runs on `stream_side`, overlapping the
- * routed path.  stream_side may be NULL or equal stream_main: then, with bf16
- * or fp8 weights and one shared expert (S = 1), the shared expert runs inside the
- * routed grouped GEMMs as one more group whose rows are all T tokens (results
- * are bitwise the same either way), and otherwise after the routed path.
+ * routed path: with fewer than 128 routed rows per expert (T*k < 128*N, a
+ * decode step, bound by streaming weights) it starts with the router, else
+ * when the routed up GEMM has ended, overlapping the routed down GEMM.
+ * stream_side may be NULL or equal stream_main: then, with bf16 or fp8 weights
+ * and one shared expert (S = 1), the shared expert runs inside the routed
+ * grouped GEMMs as one more group whose rows are all T tokens (results are
+ * bitwise the same either way), and otherwise on stream_main, before the
+ * router (T*k < 128*N) or after the routed GEMMs.
  *   x [T, d];  W_r [N, d];  b [N] nullable
  *   W1, W3 [N, I, d];  W2 [N, d, I];  s1, s3, s2 fp8 scales or NULL
  *   W1s, W3s [S*I, d];  W2s [d, S*I];  s1s, s3s, s2s   (all NULL when S = 0)
