@@ -511,6 +511,64 @@ def summarize_util(csv_path, command, out_path):
     print(text)
 
 
+def power_probe(out_path=None, reps=10):
+    """The routed expert GEMMs of the V3-shaped prefill (moe_expert_ffn: up with
+    SwiGLU, then down, on the workload's own routing) timed on the workload's
+    activations and on all-zero activations of the same shape: the same
+    instructions and memory traffic, different operand values.  Each case runs
+    0.3 s back to back before `reps` event-timed calls."""
+    import torch
+    import datagen
+    from datagen.device import upload
+    import mixture_experts_ffn_gemm_amd as moe
+    cfg = datagen.get_config("v3_prefill")
+    dev = upload(datagen.MoEInputs(cfg))
+    c = moe.config_from(cfg)
+    idx, _ = moe.router(c, dev["x"], dev["w_r"], dev["b"])
+    p = moe.permute(c, idx)
+    ex = dev["experts"]
+    rows = cfg.T * cfg.k
+    x0 = torch.zeros_like(dev["x"])
+    ws = moe.Workspace.get(c, "cuda")
+    y = torch.empty((rows, cfg.d), dtype=dev["x"].dtype, device="cuda")
+    events = HipEvents()
+    rec = events.hip.hipEventRecord
+    rec.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+    stream = torch.cuda.current_stream()
+    res = {}
+    for name, xin in (("workload activations", dev["x"]), ("zero activations", x0),
+                      ("workload activations again", dev["x"])):
+        fn = lambda: moe.expert_ffn(c, cfg.n_routed, p["offsets"], rows, xin, ex["w1"], ex["w3"],
+                                    ex["w2"], row_index=p["row_token"], y_rows=y, ws=ws)
+        t_w = time.perf_counter()
+        n = 0
+        while time.perf_counter() - t_w < 0.3:
+            fn()
+            n += 1
+            if n % 4 == 0:
+                torch.cuda.synchronize()
+        e0, e1 = events.create(2)
+        rec(e0, stream.cuda_stream)
+        for _ in range(reps):
+            fn()
+        rec(e1, stream.cuda_stream)
+        torch.cuda.synchronize()
+        res[name] = events.elapsed_ms(e0, e1) / reps
+        events.destroy([e0, e1])
+    flops = 2.0 * rows * cfg.d * 3 * cfg.inter
+    lines = ["# Routed expert GEMMs (up + SwiGLU, down) of the V3-shaped prefill, T=16384: operand-value",
+             "# dependence of their speed (same launches, same memory traffic; the clock is set by power)",
+             "# command: python bench.py --power-probe <this file>",
+             f"{'activations':30s} {'ms (up + down)':>15s} {'TFLOP/s':>9s}"]
+    for name, ms in res.items():
+        lines.append(f"{name:30s} {ms:15.3f} {flops / (ms * 1e-3) / 1e12:9.1f}")
+    text = "\n".join(lines) + "\n"
+    if out_path:
+        with open(out_path, "w") as f:
+            f.write(text)
+    print(text)
+
+
 STALL_A = ("GRBM_GUI_ACTIVE SQ_WAVE_CYCLES SQ_WAIT_ANY SQ_WAIT_INST_ANY SQ_ACTIVE_INST_ANY "
            "SQ_ACTIVE_INST_LDS SQ_ACTIVE_INST_VALU SQ_ACTIVE_INST_VMEM SQ_VALU_MFMA_BUSY_CYCLES")
 STALL_B = ("GRBM_GUI_ACTIVE SQ_WAIT_INST_LDS SQ_LDS_DATA_FIFO_FULL SQ_LDS_CMD_FIFO_FULL "
@@ -571,6 +629,11 @@ def summarize_stalls(csv_a, csv_b, command, out_path):
 def main():
     if len(sys.argv) > 1 and sys.argv[1] == "--summarize-util":
         summarize_util(sys.argv[2], sys.argv[3], sys.argv[4])
+        return
+    if len(sys.argv) > 1 and sys.argv[1] == "--power-probe":
+        import torch
+        assert torch.cuda.is_available(), "bench.py needs a GPU"
+        power_probe(sys.argv[2] if len(sys.argv) > 2 else None)
         return
     if len(sys.argv) > 1 and sys.argv[1] == "--summarize-stalls":
         summarize_stalls(sys.argv[2], sys.argv[3], sys.argv[4], sys.argv[5])
