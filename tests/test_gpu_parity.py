@@ -289,6 +289,45 @@ def test_expert_ffn_ragged_groups(lib, wdt):
         say(f"   bf16 bar {tol_for(cfg)} unreachable here: rounded pipeline alone is {ideal_err:.3e}")
 
 
+def test_expert_ffn_inter_past_zero_rows(lib):
+    """moe_expert_ffn with an intermediate width (inter_override 512) longer
+    than the workspace's zero rows (laid out for d = 256, I = 128): the rows
+    past a tile's last then repeat the last row instead of reading zeros.
+    Ragged groups against the oracle, at the bf16 bound of the ragged test."""
+    counts = [0, 1, 255, 257, 40, 300]
+    off, rows = _rows_and_offsets(counts)
+    d, I, E = 256, 512, len(counts)
+    cfg = datagen.get_config("deepseekmoe_2b", d=d, inter=128, n_routed=E, k=1, n_groups=1,
+                             topk_groups=1, T=4 * rows, n_shared=0)
+    say(f"[expert_ffn] inter_override {I} past the zero rows, counts={counts}")
+    rng = np.random.default_rng(23)
+    x = round_bf16(rng.standard_normal((rows, d)))
+    w1 = round_bf16(rng.standard_normal((E, I, d)) / np.sqrt(d))
+    w3 = round_bf16(rng.standard_normal((E, I, d)) / np.sqrt(d))
+    w2 = round_bf16(rng.standard_normal((E, d, I)) / np.sqrt(I))
+    bf = lambda a: torch.from_numpy(a.astype(np.float32)).to(torch.bfloat16).cuda()
+    c = lib.config_from(cfg)
+    row_index = np.arange(rows, dtype=np.int32)[::-1].copy()
+    y = lib.expert_ffn(c, E, torch.from_numpy(off).cuda(), rows, bf(x), bf(w1), bf(w3), bf(w2),
+                       row_index=torch.from_numpy(row_index).cuda(), inter=I)
+    torch.cuda.synchronize()
+    got = y.float().cpu().numpy()
+    xs_all = x[row_index]
+    ref = np.zeros((rows, d))
+    ideal = np.zeros((rows, d))
+    for e, n in enumerate(counts):
+        if n == 0:
+            continue
+        xs = xs_all[off[e]:off[e + 1]]
+        ref[off[e]:off[e + 1]] = oracle.swiglu(xs, w1[e], w3[e], w2[e])
+        g, u = xs @ w1[e].T, xs @ w3[e].T
+        ideal[off[e]:off[e + 1]] = round_bf16(g * oracle.sigmoid(g) * u) @ w2[e].T
+    err, ideal_err, floor = rel_err(got, ref), rel_err(round_bf16(ideal), ref), bf16_floor(ref)
+    say(f"   rel err {err:.3e} (correctly rounded bf16 pipeline: {ideal_err:.3e})")
+    assert err <= ideal_err + 0.25 * floor
+    assert err < tol_for(cfg)
+
+
 # ---------------------------------------------------------------- combine
 
 
