@@ -229,51 +229,43 @@ int run_expert_ffn(const moe_config* c, int n_experts, const int32_t* offsets, i
   dn.C = y_rows;
   dn.Nout = c->d;
   dn.K = inter;
-  // bf16: the persistent kernel takes K >= 128 (four 32-deep steps) and
-  // A byte offsets below 4 GiB; anything else goes to the 8-wave kernel.
-  // fp8: many rows per expert (prefill) take the persistent MFMA kernel with
-  // the weights dequantized to bf16 in registers; a few rows per expert
-  // (decode) the weight-streaming kernel.
-  auto persistent = [&](const GroupedGemmArgs& a, int64_t a_rows) {
-    const bool fits = a.K % 32 == 0 && a.K >= 128 &&
-                      a_rows * (int64_t)a.K * 2 < (int64_t(1) << 32) - 4096;
-    if (c->w_dtype == MOE_BF16) return fits;
-    return c->w_dtype == MOE_FP8_E4M3 && fits && a.max_rows >= 128 * (int64_t)a.n_groups;
+  // bf16: the persistent MFMA kernel (K is a multiple of 128, so at least
+  // the four 32-deep steps its pipeline has stages for).  fp8: many rows per
+  // expert (prefill) take the same kernel with the weights dequantized to
+  // bf16 in registers; a few rows per expert (decode) the weight-streaming
+  // kernel.
+  auto persistent = [&](const GroupedGemmArgs& a) {
+    if (c->w_dtype == MOE_BF16) return true;
+    return c->w_dtype == MOE_FP8_E4M3 && a.max_rows >= 128 * (int64_t)a.n_groups;
   };
-  const int64_t up_rows = row_index ? (c->T > max_rows ? c->T : max_rows) : max_rows;
   // the persistent kernels' rows past a tile's last read a row of zeros
   // (same results, less power than repeating the last row): cleared here
   const int64_t kmax = c->d > inter ? c->d : inter;
-  if (zrow && zrow_elems >= kZeroRows * kmax &&
-      (persistent(up, up_rows) || persistent(dn, max_rows))) {
+  if (zrow && zrow_elems >= kZeroRows * kmax && (persistent(up) || persistent(dn))) {
     MOE_HIP_CHECK(launch_fill_i32((int32_t*)zrow, kZeroRows * kmax / 2, 0, s));
     up.zero_row = zrow;
     dn.zero_row = zrow;
   }
-  auto bf16_gemm = [&](const GroupedGemmArgs& a, bool swiglu, int64_t a_rows) {
-    if (persistent(a, a_rows)) return launch_gemm_bf16_persist(a, swiglu, s);
-    return launch_gemm_bf16_v2(a, swiglu, s);
-  };
-  auto fp8_gemm = [&](const GroupedGemmArgs& a, bool swiglu, int64_t a_rows) {
-    if (persistent(a, a_rows)) return launch_gemm_fp8_persist(a, swiglu, s);
+  auto fp8_gemm = [&](const GroupedGemmArgs& a, bool swiglu) {
+    if (persistent(a)) return launch_gemm_fp8_persist(a, swiglu, s);
     return swiglu ? launch_gemm_fp8_swiglu(a, s) : launch_gemm_fp8_store(a, s);
   };
   MOE_HIP_CHECK(mark(ev, stage_up, false, s));
   if (c->w_dtype == MOE_F32)
     MOE_HIP_CHECK(launch_gemm_f32_swiglu(up, s));
   else if (c->w_dtype == MOE_BF16)
-    MOE_HIP_CHECK(bf16_gemm(up, true, up_rows));
+    MOE_HIP_CHECK(launch_gemm_bf16_persist(up, true, s));
   else
-    MOE_HIP_CHECK(fp8_gemm(up, true, up_rows));
+    MOE_HIP_CHECK(fp8_gemm(up, true));
   MOE_HIP_CHECK(mark(ev, stage_up, true, s));
   if (after_up) MOE_HIP_CHECK(hipEventRecord(after_up, s));
   MOE_HIP_CHECK(mark(ev, stage_dn, false, s));
   if (c->w_dtype == MOE_F32)
     MOE_HIP_CHECK(launch_gemm_f32_store(dn, s));
   else if (c->w_dtype == MOE_BF16)
-    MOE_HIP_CHECK(bf16_gemm(dn, false, max_rows));
+    MOE_HIP_CHECK(launch_gemm_bf16_persist(dn, false, s));
   else
-    MOE_HIP_CHECK(fp8_gemm(dn, false, max_rows));
+    MOE_HIP_CHECK(fp8_gemm(dn, false));
   MOE_HIP_CHECK(mark(ev, stage_dn, true, s));
   return MOE_OK;
 }

@@ -99,8 +99,6 @@ struct GroupedGemmArgs {
                             //   for rows past a tile's last (null: repeat the last row)
 };
 constexpr int kZeroRows = 16;
-// second generation: 256x256 tiles, 8 wavefronts, direct-to-LDS 4-stage pipeline
-hipError_t launch_gemm_bf16_v2(const GroupedGemmArgs& a, bool swiglu, hipStream_t s);
 // persistent: one workgroup per CU, one pipeline across all of its tiles (K >= 128)
 hipError_t launch_gemm_bf16_persist(const GroupedGemmArgs& a, bool swiglu, hipStream_t s);
 // the same with fp8 block-scaled weights, dequantized to bf16 in registers

@@ -329,6 +329,53 @@ def test_expert_ffn_inter_past_zero_rows(lib):
         assert err < tol_for(cfg)
 
 
+def test_expert_ffn_activations_past_4gib(lib):
+    """The up GEMM gathering from an activation matrix past 4 GiB (310000 rows
+    of d = 7168 bf16) through a reversed row map, so the first output rows read
+    the last x rows: 64-bit row addresses.  Sampled rows (the first, the last,
+    around the expert boundary and random ones) against the oracle."""
+    counts = [155001, 154999]
+    off, rows = _rows_and_offsets(counts)
+    d, I, E = 7168, 256, len(counts)
+    assert rows * d * 2 > 1 << 32
+    cfg = datagen.get_config("deepseekmoe_2b", d=d, inter=I, n_routed=E, k=1, n_groups=1,
+                             topk_groups=1, T=rows, n_shared=0)
+    say(f"[expert_ffn] x of {rows * d * 2 / 2**30:.2f} GiB, counts={counts}")
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(29)
+    x = torch.randn((rows, d), generator=gen, device="cuda").to(torch.bfloat16)
+    rng = np.random.default_rng(29)
+    w1 = round_bf16(rng.standard_normal((E, I, d)) / np.sqrt(d))
+    w3 = round_bf16(rng.standard_normal((E, I, d)) / np.sqrt(d))
+    w2 = round_bf16(rng.standard_normal((E, d, I)) / np.sqrt(I))
+    bf = lambda a: torch.from_numpy(a.astype(np.float32)).to(torch.bfloat16).cuda()
+    c = lib.config_from(cfg)
+    row_index = torch.arange(rows - 1, -1, -1, dtype=torch.int32, device="cuda")
+    y = lib.expert_ffn(c, E, torch.from_numpy(off).cuda(), rows, x, bf(w1), bf(w3), bf(w2),
+                       row_index=row_index)
+    torch.cuda.synchronize()
+    sample = np.unique(np.concatenate([[0, 1, rows - 1, off[1] - 1, off[1], off[1] + 1],
+                                       rng.integers(0, rows, 40)]))
+    sidx = torch.from_numpy(sample).cuda()
+    got = y[sidx].float().cpu().numpy()
+    xs = x[row_index[sidx].long()].double().cpu().numpy()
+    ref = np.zeros((len(sample), d))
+    ideal = np.zeros((len(sample), d))
+    for i, r in enumerate(sample):
+        e = int(np.searchsorted(off, r, side="right") - 1)
+        xi = xs[i:i + 1]
+        ref[i] = oracle.swiglu(xi, w1[e], w3[e], w2[e])[0]
+        g, u = xi @ w1[e].T, xi @ w3[e].T
+        ideal[i] = (round_bf16(g * oracle.sigmoid(g) * u) @ w2[e].T)[0]
+    err, ideal_err, floor = rel_err(got, ref), rel_err(round_bf16(ideal), ref), bf16_floor(ref)
+    say(f"   rel err {err:.3e} on {len(sample)} sampled rows (correctly rounded bf16 pipeline: "
+        f"{ideal_err:.3e})")
+    assert err <= ideal_err + 0.25 * floor
+    if ideal_err < tol_for(cfg):
+        assert err < tol_for(cfg)
+    del x, y
+
+
 # ---------------------------------------------------------------- combine
 
 
