@@ -482,12 +482,14 @@ def test_forward_fp8_prefill(lib):
     assert torch.equal(a, b)
 
 
-@pytest.mark.parametrize("name", ["v3_decode", "v3_prefill"])
-def test_forward_graph_replay(lib, name):
+# T = 4096 at V3 shape: T*k = 128*N, the shared expert starts after the routed
+# up GEMM; the other two start it with the router
+@pytest.mark.parametrize("name,T", [("v3_decode", None), ("v3_prefill", None), ("v3_prefill", 4096)])
+def test_forward_graph_replay(lib, name, T):
     """The forward, with its shared expert on a side stream, captured in a HIP
     graph and replayed three times with eager forwards in between: every
     replay and every eager forward equals the first eager result bitwise."""
-    cfg = small_cfg(name)
+    cfg = small_cfg(name) if T is None else small_cfg(name).replace(T=T)
     say(f"[forward-graph] {name} T={cfg.T}")
     dev = upload(datagen.MoEInputs(cfg))
     c = lib.config_from(cfg)
