@@ -185,9 +185,63 @@ def test_topk_brute_force_grouped():
         topk_groups = int(rng.integers(1, n_groups + 1))
         k = int(rng.integers(1, topk_groups * gs + 1))
         key = rng.standard_normal(n)
-        allowed, _, _ = oracle.group_limit(key[None, :], n_groups, topk_groups, 2)
+        allowed, gscore, gmargin = oracle.group_limit(key[None, :], n_groups, topk_groups, 2)
         idx, _ = oracle.topk_select(key[None, :], allowed, k)
         assert set(idx[0].tolist()) == _brute_grouped(key, n_groups, topk_groups, 2, k)
+        # group scores and the margin by brute force: the best pair sum of each
+        # group, sorted; the margin is the last kept score minus the best dropped
+        bs = sorted((max(key[a] + key[b] for a, b in itertools.combinations(range(g * gs, (g + 1) * gs), 2))
+                     for g in range(n_groups)), reverse=True)
+        assert np.allclose(np.sort(gscore[0])[::-1], bs, rtol=0, atol=1e-15)
+        if topk_groups < n_groups:
+            assert np.isclose(gmargin[0], bs[topk_groups - 1] - bs[topk_groups], rtol=0, atol=1e-15)
+        else:
+            assert np.isinf(gmargin[0])
+
+
+def test_softmax_logit_offset_hand_example(golden_dir):
+    """Softmax routing with a per-expert logit offset, worked by hand: the
+    offset moves both the selection and the gate values, the gates are the
+    unrenormalised probabilities, equal keys go to the lower index."""
+    g = _golden(golden_dir, "softmax_offset_example.json")
+    x = np.array(g["x"], np.float32)
+    wr = np.array(g["w_r"], np.float32)
+    b = np.array(g["b"], np.float32)
+    tol = g["tolerance"]
+    cfg = Cfg(n_routed=g["n_routed"], k=g["k"], gate="softmax", route_scale=g["route_scale"])
+    r = oracle.route(cfg, x.astype(np.float64), wr.astype(np.float64), b)
+    assert np.array_equal(r["z"][0] + b.astype(np.float64), np.array(g["logits_plus_offset"]))
+    assert np.allclose(r["value"][0], g["expected_p"], rtol=0, atol=tol)
+    assert r["idx"][0].tolist() == g["expected_idx"]
+    assert np.allclose(r["gates"][0], g["expected_gates"], rtol=0, atol=tol)
+    r3 = oracle.route(Cfg(n_routed=g["n_routed"], k=3, gate="softmax"), x.astype(np.float64),
+                      wr.astype(np.float64), b)
+    assert r3["idx"][0].tolist() == g["k3_expected_idx"]
+    assert np.allclose(r3["gates"][0], g["k3_expected_gates"], rtol=0, atol=tol)
+
+
+def test_softmax_offset_shift_invariance():
+    """A softmax is unchanged when every logit moves by the same amount: an
+    offset that is constant over the experts selects and gates exactly as no
+    offset, and adding a constant to a non-constant offset changes nothing;
+    the same non-constant offset does change the probabilities."""
+    rng = np.random.default_rng(12)
+    x = rng.standard_normal((200, 16))
+    wr = rng.standard_normal((10, 16)) / 4
+    cfg = Cfg(n_routed=10, k=3, gate="softmax")
+    base = oracle.route(cfg, x, wr)
+    const = oracle.route(cfg, x, wr, np.full(10, 0.75, np.float32))
+    assert np.array_equal(base["idx"], const["idx"])
+    assert np.allclose(base["gates"], const["gates"], rtol=1e-13, atol=0)
+    off = rng.normal(0, 0.5, 10).astype(np.float32)
+    a = oracle.route(cfg, x, wr, off)
+    shifted = oracle.route(cfg, x, wr, (off + np.float32(2.0)).astype(np.float32))
+    assert np.array_equal(a["idx"], shifted["idx"])
+    assert np.allclose(a["gates"], shifted["gates"], rtol=1e-6, atol=0)
+    # probabilities of softmax(z + b) by torch, as a second definition
+    p = torch.softmax(torch.from_numpy(x @ wr.T + off.astype(np.float64)), dim=1).numpy()
+    assert np.allclose(a["value"], p, rtol=1e-12, atol=0)
+    assert not np.allclose(a["value"], base["value"])
 
 
 def test_grouped_hand_example(golden_dir):
@@ -380,6 +434,44 @@ def test_stable_permutation_brute_force():
                     assert p["slot_row"][t * k + j] == row
                     row += 1
     assert row == T * k == p["offsets"][N]
+
+
+@pytest.mark.parametrize("gate", ["softmax", "sigmoid"])
+def test_idx_override_recomputes_gates(gate):
+    """forward(idx_override=...) with a selection other than the oracle's own:
+    the gates are those of the overriding experts, recomputed from the same
+    scores (aiany.app Step 2: G = p of the kept experts; open-model-atlas
+    'All 19 steps': G_i = 2.5 s_i / sum of the selected s), and the output is
+    x plus the gate-weighted textbook SwiGLU of exactly those experts."""
+    rng = np.random.default_rng(13)
+    T, d, N, I, k = 7, 8, 8, 6, 2
+    x = rng.standard_normal((T, d)).astype(np.float32)
+    wr = rng.standard_normal((N, d)).astype(np.float32)
+    ex = _rand_experts(rng, N, d, I)
+    kw = dict(route_scale=2.5) if gate == "sigmoid" else {}
+    cfg = Cfg(n_routed=N, k=k, gate=gate, **kw)
+    base = oracle.forward(cfg, x, wr, None, lambda e: ex[e], None)
+    # every token keeps its best expert and swaps its second for one it did not pick
+    over = base["idx"].copy()
+    for t in range(T):
+        over[t, 1] = next(e for e in range(N) if e not in base["idx"][t])
+    res = oracle.forward(cfg, x, wr, None, lambda e: ex[e], None, idx_override=over)
+    x64 = x.astype(np.float64)
+    z = torch.from_numpy(x64 @ wr.astype(np.float64).T)
+    if gate == "softmax":
+        want_g = np.take_along_axis(torch.softmax(z, dim=1).numpy(), over, 1)
+    else:
+        s_sel = np.take_along_axis(torch.sigmoid(z).numpy(), over, 1)
+        want_g = 2.5 * s_sel / s_sel.sum(1, keepdims=True)
+    assert np.allclose(res["gates"], want_g, rtol=1e-13, atol=0)
+    assert not np.allclose(res["gates"], base["gates"])
+    want = x64.copy()
+    for t in range(T):
+        for j in range(k):
+            e = over[t, j]
+            want[t] += want_g[t, j] * _torch_swiglu(
+                x64[t:t + 1], *(ex[e][n].astype(np.float64) for n in ("w1", "w3", "w2")))[0]
+    assert np.allclose(res["out"], want, rtol=1e-12, atol=1e-12)
 
 
 def test_idx_override_keeps_scores():
