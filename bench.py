@@ -13,7 +13,12 @@ synthetic inputs already resident in HBM.  Prints one JSON line:
   stream it runs on, against the bf16 MFMA peak;
 * decode: the fp8 decode step (T=64) as HBM GB/s over the weights of the
   experts that receive tokens, and its dominant kernel's roofline;
-* cpu_baseline: the fp64 oracle on the host cores over a bounded sample.
+* configs: the GShard (fp32), DeepSeekMoE and V2-shaped layers, each with
+  tokens/s and the layer's fraction of the MFMA peak;
+* cpu_baseline: the fp64 oracle on the host cores over a bounded sample;
+* parity (per workload, from the same CPU leg): the oracle's routing of all
+  tokens against the GPU's (near ties counted), and the output of the first
+  rows against the oracle's, relative to the RMS of the oracle's output.
 """
 from __future__ import annotations
 
@@ -153,7 +158,7 @@ def gpu_sclk_mhz():
 
 
 def run_workload(name, steps, warmup, events: HipEvents, extra=False, one_stream=False,
-                 overrides=None, graph=True):
+                 overrides=None, graph=True, check_rows=48):
     import torch
     import datagen
     from datagen.device import upload
@@ -263,8 +268,18 @@ def run_workload(name, steps, warmup, events: HipEvents, extra=False, one_stream
     events.destroy(evs)
     avg = {s: (sum(v) / len(v) if v else 0.0) for s, v in stage_ms.items()}
     counts_np = counts.cpu().numpy()
+    # the routing and the first rows of one more forward (same launch shape),
+    # for the CPU leg's comparison with the oracle
+    o2, idx2, gate2, counts2 = moe.forward(c, dev["x"], dev["w_r"], dev["b"], ex, dev["shared"],
+                                           want_routing=True,
+                                           side_stream=None if one_stream else side)
+    torch.cuda.synchronize()
+    n_check = min(cfg.T, check_rows)
+    check = dict(idx=idx2.cpu().numpy(), gate=gate2.cpu().numpy(), counts=counts2.cpu().numpy(),
+                 out=o2[:n_check].double().cpu().numpy())
+    del o2
     res = dict(cfg=cfg, elapsed=elapsed, ms_per_step=elapsed / steps * 1e3, stage_ms=avg,
-               counts=counts_np, inputs=inp, step_spread=spread, step_ms=in_order)
+               counts=counts_np, inputs=inp, step_spread=spread, step_ms=in_order, check=check)
     if extra:
         res["next_rows"] = time_next_rows(moe, c, dev, counts, events, main)
     del dev, out
@@ -280,8 +295,7 @@ FP8_PREFILL = dict(w_dtype="fp8", w_block=128)
 def fp8_prefill_summary(r):
     """Whole-forward rate and the routed up GEMM's MFMA rate (bf16 MFMAs on the
     dequantized weights) for the fp8-weight prefill."""
-    cfg = r.pop("cfg")
-    r.pop("inputs", None)
+    cfg = r["cfg"]
     flops = 2.0 * cfg.T * cfg.k * cfg.d * 2 * cfg.inter
     up_ms = r["stage_ms"]["up"]
     return {"workload": "v3_prefill with fp8 e4m3 weights + 128x128 block scales",
@@ -332,32 +346,105 @@ def decode_summary(r):
     }
 
 
-def cpu_baseline(inp, sample_tokens=48):
-    """The fp64 oracle (unchanged) on the first `sample_tokens` tokens of the
-    workload: routing of those tokens plus their routed and shared experts."""
-    import numpy as np
-    import oracle
+TOL = {"f32": 1e-4, "bf16": 2e-2, "fp8": 5e-2}  # max |gpu - oracle| / RMS(oracle out)
+TIE = 1e-6  # keys (or group scores) closer than this may select differently
+
+
+def oracle_threads() -> int:
     try:
         from threadpoolctl import threadpool_info
-        threads = max((i.get("num_threads", 1) for i in threadpool_info()), default=1)
+        return max((i.get("num_threads", 1) for i in threadpool_info()), default=1)
     except Exception:
-        threads = len(os.sched_getaffinity(0))
-    cfg = inp.cfg.replace(T=sample_tokens)
-    sub = type(inp)(cfg)  # the same seeds: rows 0..sample-1 of x are identical
-    x = sub.x()
-    wr, b = sub.router_w(), sub.router_b()
-    # generation is excluded from the timing: pre-draw the experts these tokens use
-    r = oracle.route(cfg, oracle.widen(x, cfg.act_dtype), wr.astype(np.float64), b)
-    needed = sorted(set(int(e) for e in np.unique(r["idx"])))
-    cache = {e: sub.expert(e) for e in needed}
-    shared = sub.shared()
+        return len(os.sched_getaffinity(0))
+
+
+def cpu_leg(r, timed=False):
+    """The fp64 oracle on the host cores: the benchmark's CPU leg, the only
+    place it runs the oracle.  Routes all T tokens (near-tie count, agreement
+    of the GPU's selected sets, per-expert counts and gates outside the tie
+    window), then evaluates the layer output of the first rows the GPU run
+    kept (its check forward) on the GPU's own selection (identical to the
+    oracle's outside near ties) and compares them.  With ``timed`` the wall
+    time of that output evaluation is the cpu_baseline (weight generation
+    excluded: the experts the tokens use are drawn first)."""
+    import numpy as np
+    import oracle
+    inp, cfg, chk = r["inputs"], r["cfg"], r["check"]
+    N = cfg.n_routed
+    x = inp.x()
+    wr, b = inp.router_w(), inp.router_b()
+    rt = oracle.route(cfg, oracle.widen(x, cfg.act_dtype), wr.astype(np.float64), b)
+    near = rt["margin"] < TIE
+    idx_g = chk["idx"].astype(np.int64)
+    same = np.all(np.sort(idx_g, 1) == np.sort(rt["idx"], 1), axis=1)
+    far = ~near
+    counts_ok = bool(np.array_equal(np.bincount(idx_g[far].ravel(), minlength=N),
+                                    np.bincount(rt["idx"][far].ravel(), minlength=N)))
+    go = np.take_along_axis(rt["gates"], np.argsort(rt["idx"], 1), 1)[same]
+    gg = np.take_along_axis(chk["gate"].astype(np.float64), np.argsort(idx_g, 1), 1)[same]
+    gate_err = float((np.abs(go - gg) / np.maximum(np.abs(go), 1e-3)).max(initial=0.0))
+    n = chk["out"].shape[0]
+    sub = cfg.replace(T=n)
+    xs = x[:n]
+    needed = sorted(int(e) for e in np.unique(idx_g[:n]))
+    st = inp.experts_stacked(experts=needed)
+    cache = {e: {k: (None if v is None else v[j]) for k, v in st.items()} for j, e in enumerate(needed)}
+    shared = inp.shared()
     t0 = time.perf_counter()
-    oracle.forward(cfg, x, wr, b, lambda e: cache[e], shared)
+    res = oracle.forward(sub, xs, wr, b, lambda e: cache[e], shared, idx_override=idx_g[:n])
     dt = time.perf_counter() - t0
-    return {"value": round(sample_tokens / dt, 4), "unit": "tokens/s", "cores": threads,
-            "kind": "oracle",
-            "sample": f"first {sample_tokens} tokens of {inp.cfg.name} (T={inp.cfg.T}): fp64 routing "
-                      f"and {len(needed)} routed experts + shared MLP, {dt:.1f}s"}
+    ref, got = res["out"], chk["out"]
+    rms = float(np.sqrt(np.mean(ref ** 2)))
+    rms_d = float(np.sqrt(np.mean(res["delta"] ** 2)))
+    err = float(np.abs(got - ref).max()) / rms
+    err_d = float(np.abs(got - ref).max()) / rms_d
+    import torch
+    bf = torch.from_numpy(ref.astype(np.float32)).to(torch.bfloat16).double().numpy()
+    mismatch = int((~same & far).sum())
+    tol = TOL[cfg.w_dtype]
+    parity = {"tokens_routed": int(cfg.T), "near_ties": int(near.sum()),
+              "set_mismatch_outside_ties": mismatch, "counts_equal_outside_ties": counts_ok,
+              "gate_max_rel_err": round(gate_err, 8), "output_tokens": int(n),
+              "experts_in_output_check": len(needed),
+              "err_rms_out": float(f"{err:.4e}"), "err_rms_delta": float(f"{err_d:.4e}"),
+              "tol": tol, "bf16_output_floor": float(f"{float(np.abs(bf - ref).max()) / rms:.4e}"),
+              "ok": bool(mismatch == 0 and counts_ok and gate_err < 2e-5 and err < tol)}
+    base = None
+    if timed:
+        base = {"value": round(n / dt, 4), "unit": "tokens/s", "cores": oracle_threads(),
+                "kind": "oracle",
+                "sample": f"first {n} tokens of {cfg.name} (T={cfg.T}): fp64 routing, "
+                          f"{len(needed)} routed experts + shared MLP, {dt:.1f}s"}
+    return base, parity
+
+
+# the configurations besides the V3-shaped ones, timed and checked like them:
+# GShard 16 x top-2 fp32 (aiany.app Step 2), DeepSeekMoE 1 + 63 top-7 (Step 6),
+# the V2-shaped 2 + 160 top-6 (shivam2003.com "5.6", configuration table)
+OTHER_CONFIGS = {"gshard_fp32": 512, "deepseekmoe_2b": 128, "v2_shaped": 32}  # rows checked
+MALL_BYTES = 256 << 20
+PEAK_FP32_TFLOPS = 157.3
+
+
+def config_summary(r):
+    cfg = r["cfg"]
+    ms = r["ms_per_step"]
+    flops = cfg.flops_per_token() * cfg.T
+    tflops = flops / (ms * 1e-3) / 1e12
+    wbytes = cfg.n_routed * cfg.expert_weight_bytes() + cfg.n_shared * cfg.expert_weight_bytes()
+    out = {"T": cfg.T, "d": cfg.d, "n_routed": cfg.n_routed, "n_shared": cfg.n_shared,
+           "inter": cfg.inter, "k": cfg.k, "dtype": cfg.w_dtype,
+           "ms_per_step": round(ms, 4), "tokens_per_s": round(cfg.T / (ms * 1e-3), 1),
+           "layer_tflops": round(tflops, 1),
+           "layer_frac_bf16_peak": round(tflops / PEAK_BF16_TFLOPS, 4),
+           "step_spread": r["step_spread"],
+           "stage_ms": {k: round(v, 4) for k, v in r["stage_ms"].items()},
+           "weight_bytes": wbytes,
+           "cache": ("weights fit the 256 MB Infinity Cache: resident across steps"
+                     if wbytes < MALL_BYTES else "weights exceed the 256 MB Infinity Cache: read from HBM each step")}
+    if cfg.w_dtype == "f32":
+        out["layer_frac_fp32_peak"] = round(tflops / PEAK_FP32_TFLOPS, 4)
+    return out
 
 
 def summarize_trace(path, title=""):
@@ -654,7 +741,10 @@ def main():
                     help="time eager forwards instead of replays of one captured HIP graph")
     ap.add_argument("--no-fp8-prefill", action="store_true",
                     help="skip the V3-shaped prefill with fp8 block-scaled weights")
-    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-cpu-baseline", action="store_true",
+                    help="skip the CPU leg (the oracle: cpu_baseline and the parity records)")
+    ap.add_argument("--no-configs", action="store_true",
+                    help="skip the GShard, DeepSeekMoE and V2-shaped configurations")
     ap.add_argument("--one-stream", action="store_true",
                     help="no side stream: the shared expert runs inside the routed GEMMs (bf16, S=1)")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -690,19 +780,34 @@ def main():
         "roofline": prefill_roofline(r),
         "next_rows": r.get("next_rows"),
     }
-    inp = r.pop("inputs")
+    legs = [(r, line, True)]  # (workload result, where its parity goes, timed cpu_baseline)
     if not args.no_fp8_prefill:
-        line["next_rows"]["fp8_prefill"] = fp8_prefill_summary(
-            run_workload("v3_prefill", max(2, args.steps // 2), args.warmup, events,
+        f = run_workload("v3_prefill", max(2, args.steps // 2), args.warmup, events,
                          one_stream=args.one_stream, overrides=FP8_PREFILL,
-                         graph=not args.no_graph))
+                         graph=not args.no_graph, check_rows=8)
+        line["next_rows"]["fp8_prefill"] = fp8_prefill_summary(f)
+        legs.append((f, line["next_rows"]["fp8_prefill"], False))
     if not args.no_decode:
         d = run_workload("v3_decode", args.steps, args.warmup, events, one_stream=args.one_stream,
-                         graph=not args.no_graph)
-        d.pop("inputs")
+                         graph=not args.no_graph, check_rows=16)
         line["decode"] = decode_summary(d)
+        legs.append((d, line["decode"], False))
+    if not args.no_configs:
+        line["configs"] = {}
+        for name, rows in OTHER_CONFIGS.items():
+            o = run_workload(name, args.steps, args.warmup, events, one_stream=args.one_stream,
+                             graph=not args.no_graph, check_rows=rows)
+            line["configs"][name] = config_summary(o)
+            legs.append((o, line["configs"][name], False))
     if not args.no_cpu_baseline:
-        line["cpu_baseline"] = cpu_baseline(inp)
+        for res, where, timed in legs:
+            t0 = time.time()
+            base, parity = cpu_leg(res, timed=timed)
+            where["parity"] = parity
+            if base is not None:
+                line["cpu_baseline"] = base
+            log(f"[bench] oracle leg {res['cfg'].name}{' (fp8 weights)' if res['cfg'].w_dtype == 'fp8' and res['cfg'].T > 64 else ''}: "
+                f"{time.time() - t0:.1f}s, parity ok={parity['ok']}")
     print(json.dumps(line), flush=True)
 
 

@@ -151,7 +151,10 @@ int moe_bias_update(const moe_config* cfg, float* b, const int32_t* counts, floa
  * expert-contiguous rows (the bincount and per-expert row lists of the
  * reference forward excerpt on open-model-atlas, done on the device).
  * Slot f = t*k + j.  Rows are ordered by expert, then by f.
- *   topk_idx   [T, k]   int32 in, values in [0, N)
+ *   topk_idx   [T, k]   int32 in, values in [0, N).  The values are not
+ *                       checked (that would need a host round trip); an id
+ *                       below 0 or at or above N is treated as 0 or N-1, so
+ *                       the call never reads or writes outside its buffers
  *   x          [T, d]   act_dtype, nullable (only read when x_perm != NULL)
  *   counts     [N]      int32 out: slots per expert
  *   offsets    [N+1]    int32 out: exclusive prefix sum of counts
@@ -180,11 +183,14 @@ int moe_permute(const moe_config* cfg, const int32_t* topk_idx, const void* x,
  * The shared MLP is one expert over all T rows: n_experts = 1,
  * offsets = {0, T}, inter = n_shared * inter of the layer (cfg->inter is read
  * from `inter_override` when it is > 0).
- * Experts with no rows are never read.  fp8 weights: with at least 128 rows
- * per expert on average (max_rows >= 128 * n_experts) the codes are
- * dequantized to bf16(code * scale) for bf16 MFMAs (prefill); with fewer, each
- * expert's weights are streamed once, the codes multiplied exactly and each
- * 128-wide block's fp32 partial sum scaled once (decode).
+ * Experts with no rows are never read.  fp8 weights, per projection: with at
+ * least 128 rows per expert on average (max_rows >= 128 * n_experts) and a
+ * contraction length of at least 256 (d for the up projection, inter for the
+ * down projection) the codes are dequantized to bf16(code * scale) for bf16
+ * MFMAs (prefill); otherwise each expert's weights are streamed once, the
+ * codes multiplied exactly and each 128-wide block's fp32 partial sum scaled
+ * once (decode).  The two ways round differently (the first rounds every
+ * dequantized weight to bf16) and both stay within the fp8 tolerance.
  */
 int moe_expert_ffn(const moe_config* cfg, int32_t n_experts, const int32_t* offsets,
                    int64_t max_rows, int32_t inter_override,

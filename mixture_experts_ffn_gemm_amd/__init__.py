@@ -48,7 +48,15 @@ def _stream(s=None):
 
 
 class Workspace:
-    """Device workspace grown on demand (one per device); never shrinks."""
+    """Device workspace grown on demand (one per device); never shrinks.
+
+    One cached workspace serves every call on its device that does not pass
+    its own, so such calls must be ordered (one stream, or streams the caller
+    synchronises); calls that may overlap pass separate workspaces.  Before a
+    smaller cached buffer is dropped for a larger one the device is
+    synchronised: the old buffer may still be in use by work queued on any
+    stream, and torch's caching allocator only tracks the stream that
+    allocated it."""
 
     _cache: dict = {}
 
@@ -58,6 +66,10 @@ class Workspace:
         dev = torch.device(device)
         ws = cls._cache.get(dev)
         if ws is None or ws.numel() < need:
+            if ws is not None:
+                torch.cuda.synchronize(dev)
+                cls._cache.pop(dev)
+                del ws
             ws = torch.empty(need, dtype=torch.uint8, device=dev)
             cls._cache[dev] = ws
         return ws
@@ -192,11 +204,8 @@ def combine(cfg: MoeConfig, y_perm, slot_row, topk_gate, y_shared=None, residual
     return out
 
 
-def forward(cfg: MoeConfig, x, W_r, b, experts: dict, shared=None, out=None, want_routing=False,
-            ws=None, stream=None, side_stream=None):
-    """moe_forward: the whole layer.  ``experts`` / ``shared`` are dicts with
-    w1, w3, w2 (and s1, s3, s2 for fp8).  Returns out [T, d], plus
-    (topk_idx, topk_gate, counts) when want_routing is set."""
+def _forward_args(cfg: MoeConfig, x, W_r, b, experts: dict, shared, out, want_routing):
+    """The moe_forward arguments from cfg through counts_out, and the returned tensors."""
     T, d, N, k, I, S = cfg.T, cfg.d, cfg.n_routed, cfg.k, cfg.inter, cfg.n_shared
     dev = x.device
     if out is None:
@@ -209,8 +218,7 @@ def forward(cfg: MoeConfig, x, W_r, b, experts: dict, shared=None, out=None, wan
     wd = _W[cfg.w_dtype]
     f32 = (torch.float32,)
     sh = shared or {}
-    wsp, wsn = _ws(cfg, ws, dev)
-    st = _lib.LIB.moe_forward(
+    args = (
         cfg, _p(x, "x", _ACT[cfg.act_dtype], T * d), _p(W_r, "W_r", f32, N * d),
         _p(b, "b", f32, N, optional=True),
         _p(experts["w1"], "W1", wd, N * I * d), _p(experts["w3"], "W3", wd, N * I * d),
@@ -224,7 +232,19 @@ def forward(cfg: MoeConfig, x, W_r, b, experts: dict, shared=None, out=None, wan
         _p(sh.get("s2"), "s2s", f32, optional=True),
         _p(out, "out", (_OUT[cfg.out_dtype],), T * d),
         _p(idx, "topk_idx_out", optional=True), _p(gate, "topk_gate_out", optional=True),
-        _p(counts, "counts_out", optional=True), wsp, wsn, _stream(stream),
-        _stream(side_stream) if side_stream is not None else None)
+        _p(counts, "counts_out", optional=True))
+    return args, ((out, idx, gate, counts) if want_routing else out)
+
+
+def forward(cfg: MoeConfig, x, W_r, b, experts: dict, shared=None, out=None, want_routing=False,
+            ws=None, stream=None, side_stream=None):
+    """moe_forward: the whole layer.  ``experts`` / ``shared`` are dicts with
+    w1, w3, w2 (and s1, s3, s2 for fp8).  Returns out [T, d], plus
+    (topk_idx, topk_gate, counts) when want_routing is set."""
+    args, res = _forward_args(cfg, x, W_r, b, experts, shared, out, want_routing)
+    wsp, wsn = _ws(cfg, ws, x.device)
+    st = _lib.LIB.moe_forward(*args, wsp, wsn, _stream(stream),
+                              _stream(side_stream) if side_stream is not None else None)
     _lib.check("moe_forward", st)
-    return (out, idx, gate, counts) if want_routing else out
+    return res
+

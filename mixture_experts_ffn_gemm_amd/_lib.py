@@ -12,7 +12,9 @@ import os
 from ctypes import c_float, c_int32, c_int64, c_size_t, c_void_p, c_char_p, POINTER
 
 PKG = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(PKG, "libmoe.so")
+# the in-tree build; MOE_LIBRARY may name another build of the same sources
+# (the host-sanitizer build of the tests)
+LIB_PATH = os.environ.get("MOE_LIBRARY") or os.path.join(PKG, "libmoe.so")
 
 MOE_OK, MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_HIP = 0, -1, -2, -3, -4
 DTYPES = {"f32": 0, "bf16": 1, "fp8": 2}

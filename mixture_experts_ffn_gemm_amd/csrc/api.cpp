@@ -130,6 +130,24 @@ int check_ws(const moe_config* c, void* ws, size_t ws_bytes) {
   return MOE_OK;
 }
 
+// The fork and join events of the two-stream forward: created once per host
+// thread and device on first use and kept for the life of the thread (a
+// thread enqueues one forward at a time, and a stream wait takes the event's
+// state at the time of the call, so reuse by the thread's next forward is
+// safe; per thread, so concurrent callers never share them).
+int fork_join_events(hipEvent_t* fork, hipEvent_t* join) {
+  constexpr int kMaxDev = 64;
+  thread_local hipEvent_t ev[kMaxDev][2] = {};
+  int dev = 0;
+  MOE_HIP_CHECK(hipGetDevice(&dev));
+  if (dev < 0 || dev >= kMaxDev) return fail(MOE_ERR_UNSUPPORTED, "device ordinal above 63");
+  for (int i = 0; i < 2; ++i)
+    if (!ev[dev][i]) MOE_HIP_CHECK(hipEventCreateWithFlags(&ev[dev][i], hipEventDisableTiming));
+  *fork = ev[dev][0];
+  *join = ev[dev][1];
+  return MOE_OK;
+}
+
 // Records stage event 2*stage (+1 for the end) when the caller supplied it.
 hipError_t mark(void* const* ev, int stage, bool end, hipStream_t s) {
   if (!ev || stage < 0) return hipSuccess;
@@ -232,11 +250,13 @@ int run_expert_ffn(const moe_config* c, int n_experts, const int32_t* offsets, i
   // bf16: the persistent MFMA kernel (K is a multiple of 128, so at least
   // the four 32-deep steps its pipeline has stages for).  fp8: many rows per
   // expert (prefill) take the same kernel with the weights dequantized to
-  // bf16 in registers; a few rows per expert (decode) the weight-streaming
-  // kernel.
+  // bf16 in registers, when K covers its six stages (K >= 256); a few rows
+  // per expert (decode), or K = 128, the weight-streaming kernel, which
+  // takes any row count.
   auto persistent = [&](const GroupedGemmArgs& a) {
     if (c->w_dtype == MOE_BF16) return true;
-    return c->w_dtype == MOE_FP8_E4M3 && a.max_rows >= 128 * (int64_t)a.n_groups;
+    return c->w_dtype == MOE_FP8_E4M3 && a.max_rows >= 128 * (int64_t)a.n_groups &&
+           a.K >= persist_min_k(true);
   };
   // the persistent kernels' rows past a tile's last read a row of zeros
   // (same results, less power than repeating the last row): cleared here
@@ -439,15 +459,7 @@ static int forward_impl(const moe_config* cfg, const void* x, const float* W_r, 
   const bool fold = can_fold_shared(c) && ss == sm;
   const bool two_streams = ss != sm && c.n_shared > 0;
 
-  struct Events {  // destroyed on every return path; pending events are released by HIP
-    hipEvent_t fork = nullptr, join = nullptr;
-    ~Events() {
-      if (fork) (void)hipEventDestroy(fork);
-      if (join) (void)hipEventDestroy(join);
-    }
-  } evs;
-  hipEvent_t& ev_fork = evs.fork;
-  hipEvent_t& ev_join = evs.join;
+  hipEvent_t ev_fork = nullptr, ev_join = nullptr;
   // Where the shared expert starts on the side stream.  Few rows per routed
   // expert (decode): with the router, whose phase leaves HBM idle, the
   // layer being bound by streaming weights.  Many (prefill): when the routed
@@ -455,10 +467,7 @@ static int forward_impl(const moe_config* cfg, const void* x, const float* W_r, 
   // routed up GEMM then runs alone, and the forward takes as long as when the
   // shared expert starts with the router.
   const bool fork_early = c.T * (int64_t)c.k < 128 * (int64_t)c.n_routed;
-  if (two_streams) {
-    MOE_HIP_CHECK(hipEventCreateWithFlags(&ev_fork, hipEventDisableTiming));
-    MOE_HIP_CHECK(hipEventCreateWithFlags(&ev_join, hipEventDisableTiming));
-  }
+  if (two_streams && (st = fork_join_events(&ev_fork, &ev_join))) return st;
   void* ys = nullptr;
   // shared MLP of width S * I over every token (one expert, rows {0, T})
   auto run_shared = [&]() -> int {
@@ -550,3 +559,4 @@ int moe_forward_timed(const moe_config* cfg, const void* x, const float* W_r, co
 }
 
 }  // extern "C"
+

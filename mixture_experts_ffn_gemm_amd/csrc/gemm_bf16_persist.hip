@@ -60,6 +60,8 @@
 // are then 16g + 8ks + 0..7 rather than 8(2ks + g) + 0..7; the activation
 // fragments follow the same assignment, so every MFMA still pairs equal k.
 // A step's tile is 16 KiB of activations and 8 KiB of codes.
+#include <atomic>
+
 #include "grouped_sched.h"
 #include "moe_internal.h"
 
@@ -428,12 +430,13 @@ __device__ __forceinline__ void run_tile(int& g, int nk, Issuer<BK, SWIGLU, W8>&
   constexpr int KS = G::KS, LOADS = G::LOADS;
   // row groups of four MFMAs before the barrier of a step, and the loads
   // issued after each
-  constexpr int GROUPS = 4 * (KS - 1) + 2;
+  constexpr int BARI = 2;  // row group of the last k-step before which B(g+1) sits
+  constexpr int GROUPS = 4 * (KS - 1) + BARI;
   for (int kt = 0; kt < nk; ++kt, ++g) {
     const char* cur = st[g % NS];
     char* dst = st[(g + NS - 1) % NS];
     StepScale ss_next{0.f, 0.f};
-    if (W8) {
+    if constexpr (W8) {
       // scalar loads, early: the scales of the step whose fragments the
       // barrier of this step reads
       const bool last = kt + 1 >= nk;
@@ -447,12 +450,12 @@ __device__ __forceinline__ void run_tile(int& g, int nk, Issuer<BK, SWIGLU, W8>&
 #pragma unroll
       for (int i = 0; i < MB; ++i) {
         const int grp = 4 * s + i;
-        if (s == KS - 1 && i == 2) {
+        if (s == KS - 1 && i == BARI) {
           // B(g+1), then the fragments of the next step's first k-step (fp8
           // weights: its codes, dequantized after this and the next group)
           wait_vm_lgkm<(NS - 2) * LOADS>();
           __builtin_amdgcn_s_barrier();
-          if (W8) {
+          if constexpr (W8) {
             read_w8_raw<BK, SWIGLU>(st[(g + 1) % NS], wn, lane, raw);
             read_a<BK, SWIGLU, true>(st[(g + 1) % NS], 0, wm, lane, fn);
           } else {
@@ -470,7 +473,7 @@ __device__ __forceinline__ void run_tile(int& g, int nk, Issuer<BK, SWIGLU, W8>&
             if (j >= (LOADS * grp) / GROUPS && j < upto) is.load(j, dst, wv);
           if (grp == GROUPS - 1) advance<BK, SWIGLU, W8>(is, a, tt, sc, nk, wv, lane);
         }
-        if (W8) {
+        if constexpr (W8) {
           // one column tile's dequantization per group of four MFMAs
           if (s == 0) {
             if (i == 0) read_a<BK, SWIGLU, true>(cur, 1, wm, lane, fn);
@@ -485,7 +488,7 @@ __device__ __forceinline__ void run_tile(int& g, int nk, Issuer<BK, SWIGLU, W8>&
         __builtin_amdgcn_sched_barrier(0);
       }
     }
-    if (W8) ss = ss_next;
+    if constexpr (W8) ss = ss_next;
   }
 }
 
@@ -542,8 +545,12 @@ __global__ __launch_bounds__(NTHR, 1) void gemm_bf16_persist_kernel(GroupedGemmA
     advance<BK, SWIGLU, W8>(is, args, tt, sc, nk, wv, lane);
   }
   // The row indices of the tile after the next are fetched when the issuer
-  // enters a tile and read when it enters the next one, at least NS-1 steps
-  // (one barrier) later only if a tile has NS-1 steps or more.
+  // enters a tile and read when it enters the next one.  The fetch has landed
+  // for every wave after the first wait (at most (NS-2)*LOADS newer loads
+  // outstanding) and barrier that follow NS-2 more steps of loads; the issuer
+  // enters the next tile during the step nk later, before that step's barrier,
+  // and the prologue enters tile 1 before B(0) unless nk >= NS.  So nk >= NS,
+  // which the launchers check.
   wait_vm_lgkm<(NS - 2) * G::LOADS>();
   __builtin_amdgcn_s_barrier();  // B(0)
 
@@ -551,7 +558,7 @@ __global__ __launch_bounds__(NTHR, 1) void gemm_bf16_persist_kernel(GroupedGemmA
   u32x4_t raw[NT];
   TileScale tsc{}, tsn{};
   StepScale ss{0.f, 0.f};
-  if (W8) {
+  if constexpr (W8) {
     tsc = tile_scale<SWIGLU>(args, t, wn);
     ss = step_scale(tsc, 0);
     read_w8_raw<BK, SWIGLU>(st[0], wn, lane, raw);
@@ -566,9 +573,9 @@ __global__ __launch_bounds__(NTHR, 1) void gemm_bf16_persist_kernel(GroupedGemmA
   for (int i = 0; i < sc.ntile; ++i) {
     if (i > 0) {
       t = decode_tile(tt, sc.n_groups, sc.ntn, CN, sc.tile_id(i));
-      if (W8) tsc = tsn;
+      if constexpr (W8) tsc = tsn;
     }
-    if (W8)
+    if constexpr (W8)
       tsn = i + 1 < sc.ntile
                 ? tile_scale<SWIGLU>(args, decode_tile(tt, sc.n_groups, sc.ntn, CN, sc.tile_id(i + 1)), wn)
                 : tsc;
@@ -586,24 +593,37 @@ __global__ __launch_bounds__(NTHR, 1) void gemm_bf16_persist_kernel(GroupedGemmA
   wait_vm_lgkm<0>();
 }
 
-constexpr int LIB_BK = 32, LIB_NS = 4, LIB_NS_W8 = 6;
+constexpr int LIB_BK = 32, LIB_NS = 4, LIB_BK_W8 = 32, LIB_NS_W8 = 6;
 
 }  // namespace gp
 
 int persist_grid() {
-  static int grid = [] {
-    int dev = 0, cus = 0;
-    if (hipGetDevice(&dev) != hipSuccess ||
-        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
-        cus < kNumXcd)
-      cus = 256;
-    return (cus / kNumXcd) * kNumXcd;
-  }();
-  return grid;
+  // per device: the CU count of each GPU the library runs on, read once
+  constexpr int kMaxDev = 64;
+  static std::atomic<int> grid[kMaxDev];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDev) dev = -1;
+  if (dev >= 0) {
+    const int g = grid[dev].load(std::memory_order_relaxed);
+    if (g > 0) return g;
+  }
+  int cus = 0;
+  if (dev < 0 ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+      cus < kNumXcd)
+    cus = 256;
+  const int g = (cus / kNumXcd) * kNumXcd;
+  if (dev >= 0) grid[dev].store(g, std::memory_order_relaxed);
+  return g;
+}
+
+int persist_min_k(bool fp8_weights) {
+  return fp8_weights ? gp::LIB_NS_W8 * gp::LIB_BK_W8 : gp::LIB_NS * gp::LIB_BK;
 }
 
 hipError_t launch_gemm_bf16_persist(const GroupedGemmArgs& a, bool swiglu, hipStream_t s) {
   if (a.max_rows <= 0 || a.n_groups <= 0) return hipSuccess;
+  if (a.K % gp::LIB_BK != 0 || a.K < persist_min_k(false)) return hipErrorInvalidValue;
   const int grid = persist_grid();
   if (swiglu)
     gp::gemm_bf16_persist_kernel<gp::LIB_BK, gp::LIB_NS, true, false><<<grid, gp::NTHR, 0, s>>>(a);
@@ -614,11 +634,12 @@ hipError_t launch_gemm_bf16_persist(const GroupedGemmArgs& a, bool swiglu, hipSt
 
 hipError_t launch_gemm_fp8_persist(const GroupedGemmArgs& a, bool swiglu, hipStream_t s) {
   if (a.max_rows <= 0 || a.n_groups <= 0) return hipSuccess;
+  if (a.K % gp::LIB_BK_W8 != 0 || a.K < persist_min_k(true)) return hipErrorInvalidValue;
   const int grid = persist_grid();
   if (swiglu)
-    gp::gemm_bf16_persist_kernel<gp::LIB_BK, gp::LIB_NS_W8, true, true><<<grid, gp::NTHR, 0, s>>>(a);
+    gp::gemm_bf16_persist_kernel<gp::LIB_BK_W8, gp::LIB_NS_W8, true, true><<<grid, gp::NTHR, 0, s>>>(a);
   else
-    gp::gemm_bf16_persist_kernel<gp::LIB_BK, gp::LIB_NS_W8, false, true><<<grid, gp::NTHR, 0, s>>>(a);
+    gp::gemm_bf16_persist_kernel<gp::LIB_BK_W8, gp::LIB_NS_W8, false, true><<<grid, gp::NTHR, 0, s>>>(a);
   return hipGetLastError();
 }
 

@@ -99,11 +99,18 @@ struct GroupedGemmArgs {
                             //   for rows past a tile's last (null: repeat the last row)
 };
 constexpr int kZeroRows = 16;
-// persistent: one workgroup per CU, one pipeline across all of its tiles (K >= 128)
+// Persistent: one workgroup per CU, one pipeline across all of its tiles.
+// The gathered row indices of the tile after next are read one tile after
+// they were fetched, and only a tile of at least (stages) K-steps of 32 puts
+// a wait and a barrier between the two: the launchers return
+// hipErrorInvalidValue for a smaller K.  bf16: K >= 128 (4 stages).
 hipError_t launch_gemm_bf16_persist(const GroupedGemmArgs& a, bool swiglu, hipStream_t s);
 // the same with fp8 block-scaled weights, dequantized to bf16 in registers
-// (K and Nout multiples of 128, K >= 128)
+// (K and Nout multiples of 128; 6 stages: K >= 192, so K >= 256)
 hipError_t launch_gemm_fp8_persist(const GroupedGemmArgs& a, bool swiglu, hipStream_t s);
+// the smallest K each persistent kernel accepts
+int persist_min_k(bool fp8_weights);
+// persistent grid: one workgroup per CU of the current device, a multiple of 8
 int persist_grid();
 // fp32 SIMT (act f32, w f32)
 hipError_t launch_gemm_f32_swiglu(const GroupedGemmArgs& a, hipStream_t s);

@@ -19,16 +19,22 @@
 
 namespace moe {
 
+// Expert ids outside [0, N) are clamped to 0 or N-1 wherever they address
+// memory, the same way in every kernel: a bad id then routes its slot to the
+// nearest valid expert instead of indexing past the counts, the offsets or
+// the row maps.
+__device__ __forceinline__ int clamp_expert(int e, int N) { return e < 0 ? 0 : (e >= N ? N - 1 : e); }
+
 // Wavefront-level: counts of chunk c's experts into cnt (LDS, N entries,
 // zeroed) and each slot's rank among the equal experts of the chunk.
-__device__ __forceinline__ void rank_chunk(const int32_t* __restrict__ idx, int64_t S, int c,
-                                           int* cnt, int32_t* rank) {
+__device__ __forceinline__ void rank_chunk(const int32_t* __restrict__ idx, int64_t S, int N,
+                                           int c, int* cnt, int32_t* rank) {
   const int lane = lane_id();
   const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
   for (int it = 0; it < kPermChunk / 64; ++it) {
     const int64_t f = (int64_t)c * kPermChunk + it * 64 + lane;
     const bool valid = f < S;
-    const int e = valid ? idx[f] : 0;
+    const int e = valid ? clamp_expert(idx[f], N) : 0;
     // the lanes holding the same expert, from one ballot per bit of the id
     uint64_t peers = __ballot(valid);
 #pragma unroll
@@ -60,7 +66,7 @@ __global__ __launch_bounds__(256) void permute_hist_kernel(const int32_t* __rest
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
   __builtin_amdgcn_wave_barrier();
   if (c >= nchunks) return;
-  rank_chunk(idx, S, c, cnt, rank);
+  rank_chunk(idx, S, N, c, cnt, rank);
   for (int i = lane; i < N; i += 64) hist[(int64_t)c * N + i] = cnt[i];
 }
 
@@ -77,7 +83,7 @@ __global__ __launch_bounds__(256) void permute_small_kernel(
   const int tid = threadIdx.x, w = tid >> 6;
   for (int i = tid; i < 4 * 256; i += 256) cnt[i >> 8][i & 255] = 0;
   __syncthreads();
-  if (w < nchunks) rank_chunk(idx, S, w, cnt[w], rank_s);
+  if (w < nchunks) rank_chunk(idx, S, N, w, cnt[w], rank_s);
   __syncthreads();
   int v = 0;
   if (tid < N) {
@@ -100,7 +106,7 @@ __global__ __launch_bounds__(256) void permute_small_kernel(
   }
   __syncthreads();
   for (int64_t f = tid; f < S; f += 256) {
-    const int e = idx[f];
+    const int e = clamp_expert(idx[f], N);
     const int row = s_off[e] + cnt[f / kPermChunk][e] + rank_s[f];
     row_token[row] = (int32_t)(f / k);
     slot_row[f] = row;
@@ -147,7 +153,7 @@ __global__ __launch_bounds__(256) void permute_scatter_kernel(
   }
   const int64_t f = (int64_t)blockIdx.x * kPermChunk + tid;
   if (f >= S) return;
-  const int e = idx[f];
+  const int e = clamp_expert(idx[f], N);
   const int row = s_off[e] + base[(int64_t)blockIdx.x * N + e] + rank[f];
   row_token[row] = (int32_t)(f / k);
   slot_row[f] = row;

@@ -54,13 +54,25 @@ def oracle_route(cfg, inp: datagen.MoEInputs, x=None):
     return oracle.route(cfg, x64, inp.router_w().astype(np.float64), inp.router_b())
 
 
-def check_routing(cfg, r, idx_gpu: np.ndarray, gate_gpu: np.ndarray, gate_tol=2e-5):
+def check_routing(cfg, r, idx_gpu: np.ndarray, gate_gpu: np.ndarray, gate_tol=2e-5,
+                  counts_gpu=None):
     """Selected sets equal the oracle's except for near-tie tokens, whose
-    selection must still be a valid top-k within the tie window.  Gates are
-    compared per selected expert.  Returns (near_tie_count, order_diffs)."""
+    selection must still be a valid top-k within the tie window (keys within
+    the window of the k-th, groups within the window of the last kept one, at
+    most topk_groups groups).  Per-expert counts over the other tokens equal
+    the oracle's; ``counts_gpu`` (the library's counts) must be the bincount of
+    the GPU's selection.  Gates are compared per selected expert.  Returns
+    (near_tie_count, order_diffs)."""
     T, k = idx_gpu.shape
     idx_o = r["idx"]
     near = r["margin"] < TIE
+    N = cfg.n_routed
+    if counts_gpu is not None:
+        assert np.array_equal(np.asarray(counts_gpu), np.bincount(idx_gpu.ravel(), minlength=N))
+    far = ~near
+    assert np.array_equal(np.bincount(idx_gpu[far].ravel().astype(np.int64), minlength=N),
+                          np.bincount(idx_o[far].ravel(), minlength=N)), \
+        "per-expert counts over the tokens outside the tie window differ from the oracle's"
     so, sg = np.sort(idx_o, 1), np.sort(idx_gpu.astype(np.int64), 1)
     same = np.all(so == sg, axis=1)
     bad = ~same & ~near
@@ -84,6 +96,7 @@ def check_routing(cfg, r, idx_gpu: np.ndarray, gate_gpu: np.ndarray, gate_tol=2e
             gs = cfg.n_routed // cfg.n_groups
             last = np.sort(gsc)[::-1][cfg.topk_groups - 1]
             assert np.all(gsc[idx_gpu[t] // gs] >= last - TIE), t
+            assert len(np.unique(idx_gpu[t] // gs)) <= cfg.topk_groups, t
     # gates of the agreeing tokens, matched by expert id
     oi = np.argsort(idx_o, 1)
     gi = np.argsort(idx_gpu, 1)
@@ -93,3 +106,35 @@ def check_routing(cfg, r, idx_gpu: np.ndarray, gate_gpu: np.ndarray, gate_tol=2e
     assert err.max(initial=0) < gate_tol, f"gate rel err {err.max()}"
     order_diff = int(np.sum(np.any(idx_o[same] != idx_gpu[same], axis=1)))
     return int(near.sum()), order_diff
+
+
+def expert_cache(inp: datagen.MoEInputs, experts) -> dict:
+    """The stored weights of the given routed experts, drawn on worker threads
+    (the oracle then reads them one expert at a time)."""
+    ids = sorted(set(int(e) for e in experts))
+    if not ids:
+        return {}
+    st = inp.experts_stacked(experts=ids)
+    return {e: {key: (None if v is None else v[j]) for key, v in st.items()}
+            for j, e in enumerate(ids)}
+
+
+def sample_tokens(idx: np.ndarray, n_routed: int, n_random: int, seed: int, tile: int = 256,
+                  n_experts: int = 64) -> np.ndarray:
+    """Tokens whose outputs are compared at full size: for n_experts experts
+    spread over the expert range, the tokens of the first and last row of the
+    expert's permuted rows and of the rows on either side of its first tile
+    boundary (row offset + tile - 1, offset + tile), then n_random random
+    tokens.  The permutation is the oracle's stable one of the GPU selection."""
+    T = idx.shape[0]
+    p = oracle.stable_permutation(idx.astype(np.int64), n_routed)
+    off, row_token = p["offsets"], p["row_token"]
+    picks = []
+    for e in np.linspace(0, n_routed - 1, min(n_experts, n_routed)).round().astype(int):
+        lo, hi = int(off[e]), int(off[e + 1])
+        for r in (lo, hi - 1, lo + tile - 1, lo + tile):
+            if lo <= r < hi:
+                picks.append(int(row_token[r]))
+    rng = np.random.default_rng(seed)
+    picks.extend(rng.integers(0, T, n_random).tolist())
+    return np.unique(np.array(picks, np.int64))

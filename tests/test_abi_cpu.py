@@ -118,3 +118,4 @@ def test_bias_update_argument_checks(m):
     assert L.moe_bias_update(c, p, None, 0.001, None) == -1
     assert L.moe_bias_update(c, p, p, float("nan"), None) == -1
     assert L.moe_bias_update(c, p, p, -1.0, None) == -1
+

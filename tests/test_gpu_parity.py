@@ -11,8 +11,8 @@ import torch
 import datagen
 import oracle
 from datagen.device import upload, to_torch
-from parity_util import (TIE, bf16_floor, bf16_half_ulp, check_routing, oracle_route, rel_err,
-                         round_bf16, say, tol_for)
+from parity_util import (TIE, bf16_floor, bf16_half_ulp, check_routing, expert_cache,
+                         oracle_route, rel_err, round_bf16, sample_tokens, say, tol_for)
 
 pytestmark = [pytest.mark.gpu, pytest.mark.filterwarnings("ignore::RuntimeWarning")]
 
@@ -54,17 +54,15 @@ def test_router_full_size(lib, name):
                                    None if inp.router_b() is None else to_torch(inp.router_b(), dev),
                                    want_scores=True)
     torch.cuda.synchronize()
-    near, order = check_routing(cfg, r, idx.cpu().numpy(), gate.cpu().numpy())
+    # counts through the permute: the bincount of the selection, and the
+    # oracle's over every token outside the tie window
+    p = lib.permute(c, idx)
+    torch.cuda.synchronize()
+    near, order = check_routing(cfg, r, idx.cpu().numpy(), gate.cpu().numpy(),
+                                counts_gpu=p["counts"].cpu().numpy())
     s_err = np.max(np.abs(scores.cpu().numpy() - r["value"]) / np.maximum(r["value"], 1e-6))
     say(f"   near-ties {near}/{cfg.T}, order diffs {order}, score rel err {s_err:.2e}")
     assert s_err < 2e-5
-    # counts through the permute match the oracle's bincount (outside near ties)
-    p = lib.permute(c, idx)
-    torch.cuda.synchronize()
-    counts = p["counts"].cpu().numpy()
-    assert np.array_equal(counts, np.bincount(idx.cpu().numpy().ravel(), minlength=cfg.n_routed))
-    if near == 0:
-        assert np.array_equal(counts, r["counts"])
 
 
 @pytest.mark.parametrize("name,mask_top,drop_every", [
@@ -202,6 +200,25 @@ def test_permute_bit_exact(lib, T, k, N, skew):
     assert np.array_equal(xp, x.view(torch.int16).cpu().numpy()[want["row_token"]])
 
 
+def test_permute_clamps_out_of_range_ids(lib):
+    """Expert ids below 0 or at/above N are treated as 0 or N-1 (the header's
+    contract): the permutation equals the oracle's of the clamped ids, so no
+    access leaves the counts, offsets or row maps."""
+    T, k, N = 700, 6, 160
+    rng = np.random.default_rng(77)
+    idx = np.stack([rng.choice(N, k, replace=False) for _ in range(T)]).astype(np.int32)
+    bad = rng.random(idx.shape) < 0.02
+    idx[bad] = rng.choice(np.array([-7, -1, N, N + 3, 255, 256, 1 << 20], np.int32), int(bad.sum()))
+    say(f"[permute] out-of-range ids: {int(bad.sum())} of {idx.size}")
+    cfg = datagen.get_config("v3_prefill", T=T, k=k, n_routed=N, n_groups=1, topk_groups=1,
+                             d=256, inter=128, n_shared=0)
+    res = lib.permute(lib.config_from(cfg), torch.from_numpy(idx).cuda())
+    torch.cuda.synchronize()
+    want = oracle.stable_permutation(np.clip(idx, 0, N - 1), N)
+    for key in ("counts", "offsets", "row_token", "slot_row"):
+        assert np.array_equal(res[key].cpu().numpy(), want[key]), key
+
+
 # ---------------------------------------------------------------- expert FFN
 
 
@@ -210,8 +227,8 @@ def _rows_and_offsets(counts):
     return off, int(off[-1])
 
 
-@pytest.mark.parametrize("wdt", ["f32", "bf16", "fp8", "fp8_k384", "fp8_prefill", "bf16_small_k",
-                                 "bf16_many_tiles"])
+@pytest.mark.parametrize("wdt", ["f32", "bf16", "fp8", "fp8_k384", "fp8_prefill", "fp8_prefill_d128",
+                                 "bf16_small_k", "bf16_many_tiles"])
 def test_expert_ffn_ragged_groups(lib, wdt):
     """Groups of 0, 1, tile-1, tile, tile+1 and several tiles of rows.
 
@@ -221,19 +238,23 @@ def test_expert_ffn_ragged_groups(lib, wdt):
     rows per expert on average: the weight-streaming kernel).  fp8_prefill:
     more rows per expert, the persistent MFMA kernel, whose weights are
     dequantized to bf16(code * scale); its bound models that rounding.
+    fp8_prefill_d128: the same rows with d = 128, a contraction too short for
+    that kernel's six stages: the up projection (K = d) streams its weights,
+    the down projection (K = I = 384) stays persistent.
     bf16_small_k: K = 128 for both projections, the smallest K the bf16 path
     takes (four 32-deep steps per tile, as many as the pipeline has stages).
     bf16_many_tiles: more tiles than workgroups, so every persistent workgroup
     runs its pipeline across several tiles of different experts and fills."""
-    d, I = {"f32": (256, 512), "bf16_small_k": (128, 128), "fp8_k384": (384, 512)}.get(wdt, (512, 384))
+    d, I = {"f32": (256, 512), "bf16_small_k": (128, 128), "fp8_k384": (384, 512),
+            "fp8_prefill_d128": (128, 384)}.get(wdt, (512, 384))
     counts = [0, 1, 127, 128, 129, 300, 0, 5, 64, 65]
-    if wdt == "fp8_prefill":
+    if wdt.startswith("fp8_prefill"):
         counts = [0, 1, 255, 256, 257, 600, 0, 130, 129, 300]
     if wdt == "bf16_many_tiles":
         counts = [int(c) for c in np.random.default_rng(11).integers(0, 700, 72)]
         counts[:6] = [0, 1, 255, 256, 257, 699]
     name = {"f32": "gshard_fp32", "fp8": "v3_decode", "fp8_k384": "v3_decode",
-            "fp8_prefill": "v3_decode"}.get(wdt, "deepseekmoe_2b")
+            "fp8_prefill": "v3_decode", "fp8_prefill_d128": "v3_decode"}.get(wdt, "deepseekmoe_2b")
     cfg = datagen.get_config(name, d=d, inter=I, n_routed=len(counts), k=1, n_groups=1,
                              topk_groups=1, T=sum(counts), n_shared=0)
     say(f"[expert_ffn] {wdt} d={d} I={I} counts={counts}")
@@ -263,7 +284,12 @@ def test_expert_ffn_ragged_groups(lib, wdt):
         if cfg.act_dtype == "bf16":
             # the same contraction with h stored as bf16, as the kernels store
             # it (and the dequantized weights rounded to bf16 where they are)
-            wk = tuple(round_bf16(wi) for wi in w) if wdt == "fp8_prefill" else w
+            if wdt == "fp8_prefill":
+                wk = tuple(round_bf16(wi) for wi in w)
+            elif wdt == "fp8_prefill_d128":  # only the persistent down projection rounds
+                wk = (w[0], w[1], round_bf16(w[2]))
+            else:
+                wk = w
             g, u = xs @ wk[0].T, xs @ wk[1].T
             ideal[off[e]:off[e + 1]] = round_bf16(g * oracle.sigmoid(g) * u) @ wk[2].T
     err = rel_err(got, ref)
@@ -428,21 +454,27 @@ def _run_forward(lib, cfg, dev_inputs, side=True, **kw):
     return out, idx.cpu().numpy(), gate.cpu().numpy(), counts.cpu().numpy()
 
 
-def _forward_parity(lib, cfg, tokens=None, side=True):
+def _forward_parity(lib, cfg, side=True, sample=False):
+    """The forward against the oracle: routing of every token, and the output
+    of every token (or, with ``sample``, of the tokens sample_tokens picks:
+    the first and last rows of 64 experts and the rows around their first
+    tile boundary, plus 64 random tokens)."""
     inp = datagen.MoEInputs(cfg)
     dev = upload(inp)
     out, idx, gate, counts = _run_forward(lib, cfg, dev, side=side)
+    del dev
     x = inp.x()
     r = oracle_route(cfg, inp, x)
-    near, order = check_routing(cfg, r, idx, gate)
-    assert np.array_equal(counts, np.bincount(idx.ravel(), minlength=cfg.n_routed))
-    if near == 0:
-        assert np.array_equal(counts, r["counts"])
+    near, order = check_routing(cfg, r, idx, gate, counts_gpu=counts)
+    tokens = sample_tokens(idx, cfg.n_routed, 64, cfg.seed) if sample else None
     # oracle outputs on the GPU's own selection (identical to the oracle's
     # outside near-ties; inside them any valid selection is accepted)
-    sh = inp.shared()
-    res = oracle.forward(cfg, x, inp.router_w(), inp.router_b(), inp.expert, sh, tokens=tokens,
-                         idx_override=idx)
+    used = idx if tokens is None else idx[tokens]
+    say(f"   routing checked ({near} near-ties); oracle outputs of "
+        f"{cfg.T if tokens is None else len(tokens)} tokens over {len(np.unique(used))} experts")
+    cache = expert_cache(inp, np.unique(used))
+    res = oracle.forward(cfg, x, inp.router_w(), inp.router_b(), lambda e: cache[e], inp.shared(),
+                         tokens=tokens, idx_override=idx)
     got = out.float().cpu().numpy()
     if tokens is not None:
         got = got[tokens]
@@ -461,11 +493,18 @@ def test_forward_small(lib, name):
     _forward_parity(lib, cfg)
 
 
-@pytest.mark.parametrize("name", ["gshard_fp32", "deepseekmoe_2b"])
+# the five workloads at their full sizes; the V2- and V3-shaped prefills
+# compare sampled tokens (their oracle outputs of every token would take
+# minutes), the rest every token
+@pytest.mark.timeout(600)
+@pytest.mark.parametrize("name", datagen.CONFIG_ORDER)
 def test_forward_full_size(lib, name):
     cfg = datagen.get_config(name)
-    say(f"[forward-full] {name} T={cfg.T}")
-    _forward_parity(lib, cfg)
+    sample = name in ("v2_shaped", "v3_prefill")
+    say(f"[forward-full] {name} T={cfg.T} d={cfg.d} I={cfg.inter} N={cfg.n_routed} "
+        f"w={cfg.w_dtype}{' (sampled tokens)' if sample else ''}")
+    _forward_parity(lib, cfg, sample=sample)
+    torch.cuda.empty_cache()
 
 
 def test_forward_fp8_prefill(lib):
