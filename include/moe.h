@@ -273,6 +273,38 @@ int moe_forward_timed(const moe_config* cfg, const void* x, const float* W_r, co
                       void* ws, size_t ws_bytes, void* stream_main, void* stream_side,
                       void* const* stage_events);
 
+/* Size of the static per-GPU scratch array of moe_forward_noalloc: 64 MiB,
+ * the workspace of the V3-shaped decode step (d = 7168, 1 + 256 experts,
+ * inter 2048, top-8) up to T = 256 tokens (15.2 MiB at T = 64). */
+#define MOE_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+
+/*
+ * moe_forward_noalloc - moe_forward for callers that cannot allocate device
+ * memory: code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc.  Same arguments and results as moe_forward, without
+ * ws / ws_bytes: the workspace is a static device array of
+ * MOE_NOALLOC_SCRATCH_BYTES that each GPU the library runs on holds from its
+ * first call there until the process ends.  The call itself allocates
+ * nothing (no hipMalloc, hipFree or allocating library routine); its first
+ * call on a device looks the array's address up, and the two-stream forward's
+ * fork/join events are created once per host thread and device, as in
+ * moe_forward.
+ *   Returns MOE_ERR_WORKSPACE, enqueueing nothing, when
+ *   moe_workspace_size(cfg) > MOE_NOALLOC_SCRATCH_BYTES.
+ * Every call on one GPU shares that GPU's array, which keeps the last call's
+ * contents (each call rewrites all it reads before reading it): calls that
+ * overlap on one GPU - on different streams, or from different threads
+ * without ordering between their streams - race on it.  The streams must
+ * belong to the current device.
+ */
+int moe_forward_noalloc(const moe_config* cfg, const void* x, const float* W_r, const float* b,
+                        const void* W1, const void* W3, const void* W2,
+                        const float* s1, const float* s3, const float* s2,
+                        const void* W1s, const void* W3s, const void* W2s,
+                        const float* s1s, const float* s3s, const float* s2s,
+                        void* out, int32_t* topk_idx_out, float* topk_gate_out,
+                        int32_t* counts_out, void* stream_main, void* stream_side);
+
 #ifdef __cplusplus
 }
 #endif

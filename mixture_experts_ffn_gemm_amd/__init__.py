@@ -15,11 +15,12 @@ import torch
 
 from . import _lib
 from ._lib import (MoeConfig, MoeError, config_from, make_config, status_string, last_error,
-                   version, workspace_size, EXPORTS, LIB_PATH)
+                   version, workspace_size, EXPORTS, LIB_PATH, NOALLOC_SCRATCH_BYTES)
 
 __all__ = ["MoeConfig", "MoeError", "config_from", "make_config", "status_string", "last_error",
            "version", "workspace_size", "Workspace", "router", "permute", "expert_ffn",
-           "combine", "forward", "EXPORTS", "LIB_PATH"]
+           "combine", "forward", "forward_noalloc", "EXPORTS", "LIB_PATH",
+           "NOALLOC_SCRATCH_BYTES"]
 
 _ACT = {0: (torch.float32,), 1: (torch.bfloat16, torch.int16, torch.uint16)}
 _W = {0: (torch.float32,), 1: (torch.bfloat16, torch.int16, torch.uint16),
@@ -248,3 +249,15 @@ def forward(cfg: MoeConfig, x, W_r, b, experts: dict, shared=None, out=None, wan
     _lib.check("moe_forward", st)
     return res
 
+
+def forward_noalloc(cfg: MoeConfig, x, W_r, b, experts: dict, shared=None, out=None,
+                    want_routing=False, stream=None, side_stream=None):
+    """moe_forward_noalloc: moe_forward on the library's static per-GPU scratch
+    array (no workspace argument; configs whose workspace exceeds
+    NOALLOC_SCRATCH_BYTES are rejected).  Calls that overlap on one GPU race on
+    that array.  Returns what forward() returns."""
+    args, res = _forward_args(cfg, x, W_r, b, experts, shared, out, want_routing)
+    st = _lib.LIB.moe_forward_noalloc(*args, _stream(stream),
+                                      _stream(side_stream) if side_stream is not None else None)
+    _lib.check("moe_forward_noalloc", st)
+    return res

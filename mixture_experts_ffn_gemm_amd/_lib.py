@@ -23,7 +23,7 @@ GATES = {"softmax": 0, "sigmoid": 1}
 # every symbol include/moe.h declares
 EXPORTS = ["moe_status_string", "moe_last_error", "moe_version", "moe_workspace_size",
            "moe_router", "moe_router_masked", "moe_bias_update", "moe_permute", "moe_expert_ffn",
-           "moe_combine", "moe_forward", "moe_forward_timed"]
+           "moe_combine", "moe_forward", "moe_forward_timed", "moe_forward_noalloc"]
 
 
 class MoeConfig(ctypes.Structure):
@@ -71,7 +71,13 @@ def _load():
     lib.moe_forward.argtypes = [POINTER(MoeConfig)] + [P] * 20 + [c_size_t, P, P]
     lib.moe_forward_timed.restype = ctypes.c_int
     lib.moe_forward_timed.argtypes = [POINTER(MoeConfig)] + [P] * 20 + [c_size_t, P, P, P]
+    lib.moe_forward_noalloc.restype = ctypes.c_int
+    lib.moe_forward_noalloc.argtypes = [POINTER(MoeConfig)] + [P] * 19 + [P, P]
     return lib
+
+
+# size of moe_forward_noalloc's static per-GPU scratch array (MOE_NOALLOC_SCRATCH_BYTES)
+NOALLOC_SCRATCH_BYTES = 64 << 20
 
 
 LIB = _load()

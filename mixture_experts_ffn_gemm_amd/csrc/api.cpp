@@ -1,8 +1,10 @@
 // C-ABI entry points of the MI355X DeepSeekMoE layer forward: argument
 // validation (pure host code, before any launch), workspace layout, and the
 // orchestration of the gfx950 kernels on the caller's streams.
+#include <atomic>
 #include <cmath>
 #include <cstdio>
+#include <mutex>
 #include <string>
 
 #include "../../include/moe.h"
@@ -560,3 +562,60 @@ int moe_forward_timed(const moe_config* cfg, const void* x, const float* W_r, co
 
 }  // extern "C"
 
+// ---------------------------------------------------------------- no allocation
+// The forward for callers that cannot allocate: its workspace is this static
+// array, one copy per GPU, held until the process ends.  In host code
+// `scratch` names a host-side stand-in, not device memory: its device address
+// is looked up once per device (hipGetSymbolAddress, with that device
+// current) and only that address is ever handed to a kernel.
+static __device__ __align__(256) unsigned char scratch[MOE_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+
+constexpr int kMaxScratchDev = 64;
+std::atomic<void*> g_scratch_ptr[kMaxScratchDev];
+std::mutex g_scratch_mu;
+
+// The current device's copy of `scratch`, looked up on the first call there.
+int scratch_for_current_device(void** out) {
+  int dev = 0;
+  MOE_HIP_CHECK(hipGetDevice(&dev));
+  if (dev < 0 || dev >= kMaxScratchDev) return fail(MOE_ERR_UNSUPPORTED, "device ordinal above 63");
+  void* p = g_scratch_ptr[dev].load(std::memory_order_acquire);
+  if (!p) {
+    std::lock_guard<std::mutex> lk(g_scratch_mu);
+    p = g_scratch_ptr[dev].load(std::memory_order_relaxed);
+    if (!p) {
+      MOE_HIP_CHECK(hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)));
+      if (!p) return fail(MOE_ERR_HIP, "hipGetSymbolAddress(scratch) gave a null address");
+      g_scratch_ptr[dev].store(p, std::memory_order_release);
+    }
+  }
+  *out = p;
+  return MOE_OK;
+}
+
+}  // namespace
+
+extern "C" int moe_forward_noalloc(const moe_config* cfg, const void* x, const float* W_r,
+                                   const float* b, const void* W1, const void* W3, const void* W2,
+                                   const float* s1, const float* s3, const float* s2,
+                                   const void* W1s, const void* W3s, const void* W2s,
+                                   const float* s1s, const float* s3s, const float* s2s, void* out,
+                                   int32_t* topk_idx_out, float* topk_gate_out,
+                                   int32_t* counts_out, void* stream_main, void* stream_side) {
+  g_err.clear();
+  int st = check_config(cfg);
+  if (st) return st;
+  const size_t need = make_layout(*cfg).total;
+  if (need > (size_t)MOE_NOALLOC_SCRATCH_BYTES)
+    return fail(MOE_ERR_WORKSPACE, "this config needs " + std::to_string(need) +
+                                       " bytes of workspace; moe_forward_noalloc has " +
+                                       std::to_string((size_t)MOE_NOALLOC_SCRATCH_BYTES) +
+                                       " (use moe_forward with a workspace)");
+  void* ws = nullptr;
+  if (cfg->T > 0 && (st = scratch_for_current_device(&ws))) return st;
+  return forward_impl(cfg, x, W_r, b, W1, W3, W2, s1, s3, s2, W1s, W3s, W2s, s1s, s3s, s2s, out,
+                      topk_idx_out, topk_gate_out, counts_out, ws, MOE_NOALLOC_SCRATCH_BYTES,
+                      stream_main, stream_side, nullptr);
+}

@@ -119,3 +119,19 @@ def test_bias_update_argument_checks(m):
     assert L.moe_bias_update(c, p, p, float("nan"), None) == -1
     assert L.moe_bias_update(c, p, p, -1.0, None) == -1
 
+
+def test_noalloc_forward_rejects_configs_beyond_its_scratch(m):
+    """moe_forward_noalloc refuses, before touching the device, a config whose
+    workspace exceeds its static scratch array; the V3-shaped decode step fits."""
+    L = m._lib.LIB
+    dec = m.config_from(datagen.get_config("v3_decode"))
+    assert 0 < m.workspace_size(dec) <= m.NOALLOC_SCRATCH_BYTES
+    big = m.config_from(datagen.get_config("v3_prefill"))
+    assert m.workspace_size(big) > m.NOALLOC_SCRATCH_BYTES
+    p = 0x1000
+    assert L.moe_forward_noalloc(big, *([p] * 19), None, None) == -3
+    assert "moe_forward_noalloc has" in m.last_error()
+    hdr = open(os.path.join(ROOT, "include", "moe.h")).read()
+    assert re.search(r"#define MOE_NOALLOC_SCRATCH_BYTES \(\(size_t\)64 << 20\)", hdr)
+    assert m.NOALLOC_SCRATCH_BYTES == 64 << 20
+    assert L.moe_forward_noalloc(None, *([None] * 19), None, None) == -1
