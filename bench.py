@@ -157,7 +157,16 @@ def gpu_sclk_mhz():
     return found[0] if len(found) == 1 else None
 
 
-def run_workload(name, steps, warmup, events: HipEvents, extra=False, one_stream=False,
+def shared_placement(cfg, two_streams: bool) -> str:
+    """How the timed forward runs the shared expert: folded into the routed
+    grouped GEMMs as one more group (one stream; bf16 or fp8 weights and one
+    shared expert), else on a second stream."""
+    if not two_streams and cfg.n_shared == 1 and cfg.w_dtype in ("bf16", "fp8"):
+        return "folded"
+    return "side stream" if cfg.n_shared > 0 else "none"
+
+
+def run_workload(name, steps, warmup, events: HipEvents, extra=False, two_streams=False,
                  overrides=None, graph=True, check_rows=48):
     import torch
     import datagen
@@ -174,6 +183,8 @@ def run_workload(name, steps, warmup, events: HipEvents, extra=False, one_stream
     out = torch.empty((cfg.T, cfg.d), dtype=torch.float32, device="cuda")
     counts = torch.empty(cfg.n_routed, dtype=torch.int32, device="cuda")
     main = torch.cuda.current_stream()
+    placement = shared_placement(cfg, two_streams)
+    one_stream = placement == "folded"
     side = main if one_stream else torch.cuda.Stream()
     L = moe._lib.LIB
     ex, sh = dev["experts"], dev["shared"] or {}
@@ -279,7 +290,8 @@ def run_workload(name, steps, warmup, events: HipEvents, extra=False, one_stream
                  out=o2[:n_check].double().cpu().numpy())
     del o2
     res = dict(cfg=cfg, elapsed=elapsed, ms_per_step=elapsed / steps * 1e3, stage_ms=avg,
-               counts=counts_np, inputs=inp, step_spread=spread, step_ms=in_order, check=check)
+               counts=counts_np, inputs=inp, step_spread=spread, step_ms=in_order, check=check,
+               shared_expert=placement)
     if extra:
         res["next_rows"] = time_next_rows(moe, c, dev, counts, events, main)
     del dev, out
@@ -296,9 +308,10 @@ def fp8_prefill_summary(r):
     """Whole-forward rate and the routed up GEMM's MFMA rate (bf16 MFMAs on the
     dequantized weights) for the fp8-weight prefill."""
     cfg = r["cfg"]
-    flops = 2.0 * cfg.T * cfg.k * cfg.d * 2 * cfg.inter
+    flops = 2.0 * up_rows(r) * cfg.d * 2 * cfg.inter
     up_ms = r["stage_ms"]["up"]
     return {"workload": "v3_prefill with fp8 e4m3 weights + 128x128 block scales",
+            "shared_expert": r["shared_expert"],
             "ms_per_step": round(r["ms_per_step"], 4),
             "tokens_per_s": round(cfg.T / (r["ms_per_step"] * 1e-3), 1),
             "up_ms": round(up_ms, 4), "down_ms": round(r["stage_ms"]["down"], 4),
@@ -307,16 +320,26 @@ def fp8_prefill_summary(r):
             "up_frac_bf16_peak": round(flops / (up_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)}
 
 
+def up_rows(r):
+    """Rows of the up-projection launch: the T*k routed slots, plus the T
+    tokens of the shared expert when it is folded in as one more group."""
+    cfg = r["cfg"]
+    return cfg.T * cfg.k + (cfg.T if r["shared_expert"] == "folded" else 0)
+
+
 def prefill_roofline(r):
     cfg = r["cfg"]
-    flops = 2.0 * cfg.T * cfg.k * cfg.d * 2 * cfg.inter  # W1 and W3 over all T*k routed rows
+    flops = 2.0 * up_rows(r) * cfg.d * 2 * cfg.inter  # W1 and W3 over every row of the launch
     ms = r["stage_ms"]["up"]
     achieved = flops / (ms * 1e-3) / 1e12
-    return {"bound": "mfma", "kernel": "gp::gemm_bf16_persist_kernel<32, 4, true, false> (routed W1|W3 + SwiGLU)",
+    what = "routed + folded shared W1|W3" if r["shared_expert"] == "folded" else "routed W1|W3"
+    return {"bound": "mfma", "kernel": f"gp::gemm_bf16_persist_kernel<32, 4, true, false> ({what} + SwiGLU)",
+            "rows_per_launch": up_rows(r),
             "achieved": round(achieved, 1), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
             "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
             "algorithmic_per_launch": flops, "avg_launch_ms": round(ms, 4),
-            "traffic": traffic_from_profile("prefill_up", ["gemm_bf16_persist.hip", "grouped_sched.h"], flops)}
+            "traffic": traffic_from_profile("prefill_up" + ("_folded" if r["shared_expert"] == "folded" else ""),
+                                            ["gemm_bf16_persist.hip", "grouped_sched.h"], flops)}
 
 
 def decode_summary(r):
@@ -327,12 +350,15 @@ def decode_summary(r):
     total_bytes = (n_active + cfg.n_shared) * per_expert
     ms = r["ms_per_step"]
     gbps = total_bytes / (ms * 1e-3) / 1e9
-    # dominant kernel: routed fp8 W1|W3 stream (2/3 of the active weight bytes)
-    up_bytes = n_active * (2 * cfg.d * cfg.inter + 2 * (cfg.d // 128) * (cfg.inter // 128) * 4)
+    # dominant kernel: the fp8 W1|W3 stream (2/3 of the active weight bytes) of the
+    # active routed experts, and of the shared expert when it is folded in
+    streamed = n_active + (cfg.n_shared if r["shared_expert"] == "folded" else 0)
+    up_bytes = streamed * (2 * cfg.d * cfg.inter + 2 * (cfg.d // 128) * (cfg.inter // 128) * 4)
     up_ms = r["stage_ms"]["up"]
     up_gbps = up_bytes / (up_ms * 1e-3) / 1e9
     return {
-        "workload": cfg.name, "T": cfg.T, "ms_per_step": round(ms, 4),
+        "workload": cfg.name, "T": cfg.T, "shared_expert": r["shared_expert"],
+        "ms_per_step": round(ms, 4),
         "hbm_GBps": round(gbps, 1), "hbm_frac": round(gbps / PEAK_HBM_GBPS, 4),
         "n_active_routed": n_active, "idle_experts": int(cfg.n_routed - n_active),
         "weight_bytes_per_step": total_bytes, "step_spread": r["step_spread"],
@@ -341,8 +367,9 @@ def decode_summary(r):
                      "achieved": round(up_gbps, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
                      "frac": round(up_gbps / PEAK_HBM_GBPS, 4), "algorithmic_per_launch": up_bytes,
                      "avg_launch_ms": round(up_ms, 4),
-                     "traffic": traffic_from_profile("decode_up", ["gemm_fp8.hip", "grouped_sched.h"],
-                                                     up_bytes)},
+                     "traffic": traffic_from_profile(
+                         "decode_up" + ("_folded" if r["shared_expert"] == "folded" else ""),
+                         ["gemm_fp8.hip", "grouped_sched.h"], up_bytes)},
     }
 
 
@@ -433,7 +460,7 @@ def config_summary(r):
     tflops = flops / (ms * 1e-3) / 1e12
     wbytes = cfg.n_routed * cfg.expert_weight_bytes() + cfg.n_shared * cfg.expert_weight_bytes()
     out = {"T": cfg.T, "d": cfg.d, "n_routed": cfg.n_routed, "n_shared": cfg.n_shared,
-           "inter": cfg.inter, "k": cfg.k, "dtype": cfg.w_dtype,
+           "inter": cfg.inter, "k": cfg.k, "dtype": cfg.w_dtype, "shared_expert": r["shared_expert"],
            "ms_per_step": round(ms, 4), "tokens_per_s": round(cfg.T / (ms * 1e-3), 1),
            "layer_tflops": round(tflops, 1),
            "layer_frac_bf16_peak": round(tflops / PEAK_BF16_TFLOPS, 4),
@@ -483,7 +510,7 @@ def copy_calibration():
     del src, dst
 
 
-def summarize_pmc(fetch_csv, write_csv, command):
+def summarize_pmc(fetch_csv, write_csv, command, folded=True):
     """Per-launch HBM traffic of the routed W1|W3 GEMMs from two rocprofv3
     --pmc runs of the same bench command (FETCH_SIZE, then WRITE_SIZE, KiB per
     dispatch), each scaled by what the counter reads for the calibration copy.
@@ -517,8 +544,10 @@ def summarize_pmc(fetch_csv, write_csv, command):
     cal_w = pick(write, lambda n: "MulFunctor" in n)
     sf = COPY_CAL_BYTES / fetch[cal_f]
     sw = COPY_CAL_BYTES / write[cal_w]
-    db = {"calibration": {"copy_bytes": COPY_CAL_BYTES, "fetch_counter_bytes": fetch[cal_f],
-                          "write_counter_bytes": write[cal_w], "fetch_scale": sf, "write_scale": sw}}
+    db = read_traffic_db()  # entries of the other shared-expert placement are kept
+    db["calibration"] = {"copy_bytes": COPY_CAL_BYTES, "fetch_counter_bytes": fetch[cal_f],
+                         "write_counter_bytes": write[cal_w], "fetch_scale": sf, "write_scale": sw}
+    suffix = "_folded" if folded else ""
     targets = {
         "prefill_up": (lambda n: "gemm_bf16_persist_kernel<32, 4, true, false>" in n,
                        ["gemm_bf16_persist.hip", "grouped_sched.h"]),
@@ -529,15 +558,19 @@ def summarize_pmc(fetch_csv, write_csv, command):
         if kf is None or kw is None:
             continue
         fb, wb = fetch[kf] * sf, write[kw] * sw
-        db[key] = {"kernel": kf[0], "grid": kf[1], "fetch_bytes": round(fb), "write_bytes": round(wb),
-                   "hbm_bytes_per_launch": round(fb + wb), "source_digest": source_digest(*sources)}
+        db[key + suffix] = {"kernel": kf[0], "grid": kf[1], "fetch_bytes": round(fb),
+                            "write_bytes": round(wb), "hbm_bytes_per_launch": round(fb + wb),
+                            "shared_expert": "folded into the launch" if folded else "side stream",
+                            "source_digest": source_digest(*sources)}
     header = ("# HBM traffic per launch of the routed W1|W3 GEMMs (rocprofv3 --pmc, two runs)\n"
               f"# command (run from /tmp, TMPDIR=/tmp), once with FETCH_SIZE and once with WRITE_SIZE:\n"
               f"#   {command}\n"
               "# each counter is scaled by its reading for a plain fp32 copy of "
               f"{COPY_CAL_BYTES >> 20} MiB read + {COPY_CAL_BYTES >> 20} MiB written\n"
               "# prefill_up = V3-shaped prefill (T=16384) routed up launch, decode_up = fp8 decode "
-              "(T=64) routed up launch; source_digest pins the kernel sources\n")
+              "(T=64) routed up launch; *_folded = the same launches with the shared expert folded in as\n"
+              "# one more group (bench.py's default), the others with it on a second stream (--two-streams);\n"
+              "# source_digest pins the kernel sources\n")
     with open(TRAFFIC_FILE, "w") as f:
         f.write(header)
         f.write(json.dumps(db, indent=1) + "\n")
@@ -560,10 +593,12 @@ def summarize_util(csv_path, command, out_path):
         names[key] = r["Kernel_Name"]
         dur[key] = int(r["End_Timestamp"]) - int(r["Start_Timestamp"])
     n_xcd, simds = 8, 256 * 4
-    targets = {"bf16 routed up (prefill)": "gemm_bf16_persist_kernel<32, 4, true, false>",
-               "bf16 routed down (prefill)": "gemm_bf16_persist_kernel<32, 4, false, false>",
-               "fp8-weight routed up (prefill)": "gemm_bf16_persist_kernel<32, 6, true, true>",
-               "fp8 routed up (decode)": "gemm_fp8_small_kernel<true, 4, 2>"}
+    targets = {"bf16 up (prefill)": "gemm_bf16_persist_kernel<32, 4, true, false>",
+               "bf16 down (prefill)": "gemm_bf16_persist_kernel<32, 4, false, false>",
+               "fp8-weight up (prefill)": "gemm_bf16_persist_kernel<32, 6, true, true>",
+               "fp8-weight down (prefill)": "gemm_bf16_persist_kernel<32, 6, false, true>",
+               "fp8 up (decode)": "gemm_fp8_small_kernel<true, 4, 2>",
+               "fp8 down (decode)": "gemm_fp8_small_kernel<false, 2, 3>"}
     lines = ["# MFMA utilisation of the main GEMM launches (rocprofv3 --pmc, one run)",
              "# command (run from /tmp, TMPDIR=/tmp):",
              f"#   {command}",
@@ -656,6 +691,71 @@ def power_probe(out_path=None, reps=10):
     print(text)
 
 
+def padding_probe(out_path=None, reps=10):
+    """The routed expert GEMMs of the V3-shaped prefill (moe_expert_ffn: up with
+    SwiGLU, then down) on the workload's own routing, and on the same rows
+    regrouped so that every expert owns exactly T*k/N = 512 of them (no
+    partly filled 256-row tile): the same flops, gathers and weights, without
+    the padding rows.  Each case runs 0.3 s back to back before `reps`
+    event-timed calls."""
+    import torch
+    import datagen
+    from datagen.device import upload
+    import mixture_experts_ffn_gemm_amd as moe
+    cfg = datagen.get_config("v3_prefill")
+    dev = upload(datagen.MoEInputs(cfg), shared=False)
+    c = moe.config_from(cfg)
+    idx, _ = moe.router(c, dev["x"], dev["w_r"], dev["b"])
+    p = moe.permute(c, idx)
+    ex = dev["experts"]
+    rows = cfg.T * cfg.k
+    per = rows // cfg.n_routed
+    uniform = torch.arange(0, rows + 1, per, dtype=torch.int32, device="cuda")
+    counts = p["counts"].cpu().numpy()
+    tiles_real = int(sum(-(-int(n) // 256) for n in counts))
+    ws = moe.Workspace.get(c, "cuda")
+    y = torch.empty((rows, cfg.d), dtype=dev["x"].dtype, device="cuda")
+    events = HipEvents()
+    rec = events.hip.hipEventRecord
+    rec.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+    stream = torch.cuda.current_stream()
+    res = {}
+    for name, off in (("workload routing", p["offsets"]), ("512 rows per expert", uniform),
+                      ("workload routing again", p["offsets"])):
+        fn = lambda: moe.expert_ffn(c, cfg.n_routed, off, rows, dev["x"], ex["w1"], ex["w3"],
+                                    ex["w2"], row_index=p["row_token"], y_rows=y, ws=ws)
+        t_w = time.perf_counter()
+        n = 0
+        while time.perf_counter() - t_w < 0.3:
+            fn()
+            n += 1
+            if n % 4 == 0:
+                torch.cuda.synchronize()
+        e0, e1 = events.create(2)
+        rec(e0, stream.cuda_stream)
+        for _ in range(reps):
+            fn()
+        rec(e1, stream.cuda_stream)
+        torch.cuda.synchronize()
+        res[name] = events.elapsed_ms(e0, e1) / reps
+        events.destroy([e0, e1])
+    flops = 2.0 * rows * cfg.d * 3 * cfg.inter
+    lines = ["# Routed expert GEMMs (up + SwiGLU, down) of the V3-shaped prefill, T=16384: the cost of",
+             "# partly filled 256-row tiles.  Same flops, gathered rows and weights; the second case",
+             "# regroups the rows so every expert owns exactly 512 (no padding tile)",
+             "# command: python bench.py --padding-probe <this file>",
+             f"# M-tiles: workload routing {tiles_real} (counts min {counts.min()}, max {counts.max()}), "
+             f"512 rows per expert {rows // 256}: {tiles_real / (rows // 256):.3f}x",
+             f"{'rows per expert':30s} {'ms (up + down)':>15s} {'TFLOP/s':>9s}"]
+    for name, ms in res.items():
+        lines.append(f"{name:30s} {ms:15.3f} {flops / (ms * 1e-3) / 1e12:9.1f}")
+    text = "\n".join(lines) + "\n"
+    if out_path:
+        with open(out_path, "w") as f:
+            f.write(text)
+    print(text)
+
+
 STALL_A = ("GRBM_GUI_ACTIVE SQ_WAVE_CYCLES SQ_WAIT_ANY SQ_WAIT_INST_ANY SQ_ACTIVE_INST_ANY "
            "SQ_ACTIVE_INST_LDS SQ_ACTIVE_INST_VALU SQ_ACTIVE_INST_VMEM SQ_VALU_MFMA_BUSY_CYCLES")
 STALL_B = ("GRBM_GUI_ACTIVE SQ_WAIT_INST_LDS SQ_LDS_DATA_FIFO_FULL SQ_LDS_CMD_FIFO_FULL "
@@ -722,6 +822,11 @@ def main():
         assert torch.cuda.is_available(), "bench.py needs a GPU"
         power_probe(sys.argv[2] if len(sys.argv) > 2 else None)
         return
+    if len(sys.argv) > 1 and sys.argv[1] == "--padding-probe":
+        import torch
+        assert torch.cuda.is_available(), "bench.py needs a GPU"
+        padding_probe(sys.argv[2] if len(sys.argv) > 2 else None)
+        return
     if len(sys.argv) > 1 and sys.argv[1] == "--summarize-stalls":
         summarize_stalls(sys.argv[2], sys.argv[3], sys.argv[4], sys.argv[5])
         return
@@ -729,7 +834,9 @@ def main():
         summarize_trace(sys.argv[2], sys.argv[3] if len(sys.argv) > 3 else "")
         return
     if len(sys.argv) > 1 and sys.argv[1] == "--summarize-pmc":
-        summarize_pmc(sys.argv[2], sys.argv[3], sys.argv[4] if len(sys.argv) > 4 else "")
+        # --summarize-pmc FETCH_CSV WRITE_CSV COMMAND [two-streams]
+        summarize_pmc(sys.argv[2], sys.argv[3], sys.argv[4] if len(sys.argv) > 4 else "",
+                      folded=not (len(sys.argv) > 5 and sys.argv[5] == "two-streams"))
         return
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -745,8 +852,9 @@ def main():
                     help="skip the CPU leg (the oracle: cpu_baseline and the parity records)")
     ap.add_argument("--no-configs", action="store_true",
                     help="skip the GShard, DeepSeekMoE and V2-shaped configurations")
-    ap.add_argument("--one-stream", action="store_true",
-                    help="no side stream: the shared expert runs inside the routed GEMMs (bf16, S=1)")
+    ap.add_argument("--two-streams", action="store_true",
+                    help="run the shared expert on a second stream instead of folding it into the "
+                         "routed GEMMs (by default folded where it can be: bf16/fp8, one shared expert)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="launch a known-size copy first (scale for PMC byte counters)")
     args = ap.parse_args()
@@ -761,7 +869,7 @@ def main():
     if args.copy_calibration:
         copy_calibration()
     r = run_workload(args.workload, args.steps, args.warmup, events, extra=True,
-                     one_stream=args.one_stream, graph=not args.no_graph)
+                     two_streams=args.two_streams, graph=not args.no_graph)
     cfg = r["cfg"]
     value = cfg.T * args.steps / r["elapsed"]
     flops = cfg.flops_per_token() * cfg.T
@@ -773,7 +881,8 @@ def main():
         "launch": "eager" if args.no_graph else "hip graph replay",
         "config": {"workload": cfg.name, "T": cfg.T, "d": cfg.d, "n_routed": cfg.n_routed,
                    "n_shared": cfg.n_shared, "inter": cfg.inter, "k": cfg.k,
-                   "groups": f"{cfg.topk_groups}/{cfg.n_groups}", "gate": cfg.gate},
+                   "groups": f"{cfg.topk_groups}/{cfg.n_groups}", "gate": cfg.gate,
+                   "shared_expert": r["shared_expert"]},
         "layer_mfma_frac": round(flops / (r["ms_per_step"] * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
         "step_spread": r["step_spread"],
         "stage_ms": {k: round(v, 4) for k, v in r["stage_ms"].items()},
@@ -783,19 +892,19 @@ def main():
     legs = [(r, line, True)]  # (workload result, where its parity goes, timed cpu_baseline)
     if not args.no_fp8_prefill:
         f = run_workload("v3_prefill", max(2, args.steps // 2), args.warmup, events,
-                         one_stream=args.one_stream, overrides=FP8_PREFILL,
+                         two_streams=args.two_streams, overrides=FP8_PREFILL,
                          graph=not args.no_graph, check_rows=8)
         line["next_rows"]["fp8_prefill"] = fp8_prefill_summary(f)
         legs.append((f, line["next_rows"]["fp8_prefill"], False))
     if not args.no_decode:
-        d = run_workload("v3_decode", args.steps, args.warmup, events, one_stream=args.one_stream,
+        d = run_workload("v3_decode", args.steps, args.warmup, events, two_streams=args.two_streams,
                          graph=not args.no_graph, check_rows=16)
         line["decode"] = decode_summary(d)
         legs.append((d, line["decode"], False))
     if not args.no_configs:
         line["configs"] = {}
         for name, rows in OTHER_CONFIGS.items():
-            o = run_workload(name, args.steps, args.warmup, events, one_stream=args.one_stream,
+            o = run_workload(name, args.steps, args.warmup, events, two_streams=args.two_streams,
                              graph=not args.no_graph, check_rows=rows)
             line["configs"][name] = config_summary(o)
             legs.append((o, line["configs"][name], False))

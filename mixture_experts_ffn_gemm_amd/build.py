@@ -29,6 +29,10 @@ HIPCC_FLAGS = [
 ]
 
 
+# roctx ranges around the forward's stages (rocprofiler-sdk's marker library)
+LINK_LIBS = ["-L/opt/rocm/lib", "-lrocprofiler-sdk-roctx", "-Wl,-rpath,/opt/rocm/lib"]
+
+
 def hipcc() -> str:
     for cand in (os.environ.get("HIPCC"), "/opt/rocm/bin/hipcc", shutil.which("hipcc")):
         if cand and os.path.exists(cand):
@@ -60,7 +64,7 @@ def build(verbose: bool = False) -> str:
     with ThreadPoolExecutor(min(8, len(srcs))) as ex:
         objs = list(ex.map(compile_one, srcs))
     tmp = LIB + ".tmp"
-    cmd = [cc, "-shared", f"--offload-arch={ARCH}", "-o", tmp, *objs]
+    cmd = [cc, "-shared", f"--offload-arch={ARCH}", "-o", tmp, *objs, *LINK_LIBS]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stderr}")

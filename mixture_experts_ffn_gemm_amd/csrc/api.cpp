@@ -7,6 +7,8 @@
 #include <mutex>
 #include <string>
 
+#include <rocprofiler-sdk-roctx/roctx.h>
+
 #include "../../include/moe.h"
 #include "moe_internal.h"
 
@@ -150,12 +152,28 @@ int fork_join_events(hipEvent_t* fork, hipEvent_t* join) {
   return MOE_OK;
 }
 
-// Records stage event 2*stage (+1 for the end) when the caller supplied it.
+// Stage boundaries of the forward: a roctx range per stage on the host (seen
+// by rocprofv3 --marker-trace; host-side only, so graph capture records
+// nothing of them), and stage event 2*stage (+1 for the end) when the caller
+// supplied it.  A range is left open only when a launch fails in between.
+const char* const kStageNames[MOE_NUM_STAGES] = {"moe router", "moe permute", "moe routed up",
+                                                 "moe routed down", "moe shared up",
+                                                 "moe shared down", "moe combine"};
+
 hipError_t mark(void* const* ev, int stage, bool end, hipStream_t s) {
-  if (!ev || stage < 0) return hipSuccess;
+  if (stage < 0) return hipSuccess;
+  if (end) roctxRangePop();
+  else roctxRangePushA(kStageNames[stage]);
+  if (!ev) return hipSuccess;
   void* e = ev[2 * stage + (end ? 1 : 0)];
   return e ? hipEventRecord((hipEvent_t)e, s) : hipSuccess;
 }
+
+// The roctx range of one whole forward, closed on every return path.
+struct ForwardRange {
+  ForwardRange() { roctxRangePushA("moe_forward"); }
+  ~ForwardRange() { roctxRangePop(); }
+};
 
 template <typename P>
 P* at(void* ws, size_t off) {
@@ -455,6 +473,7 @@ static int forward_impl(const moe_config* cfg, const void* x, const float* W_r, 
       return fail(MOE_ERR_INVALID_ARG, "fp8 shared weights need s1s, s3s, s2s");
   }
   if ((st = check_ws(cfg, ws, ws_bytes))) return st;
+  const ForwardRange range;
   const Layout L = make_layout(c);
   hipStream_t sm = (hipStream_t)stream_main;
   hipStream_t ss = stream_side ? (hipStream_t)stream_side : sm;

@@ -13,8 +13,12 @@
 // one workgroup per CU.  The tile list is cut into one contiguous range per
 // XCD, and the workgroups of an XCD take its tiles round-robin, so at any time
 // an XCD works on consecutive tiles that share weight panels and activation
-// rows through its L2.  Every workgroup rebuilds the per-expert tile prefix
-// from the device offsets in LDS; the host never waits for the counts.
+// rows through its L2.  A shared expert folded in as the last group is not
+// part of that cut: each XCD takes an eighth of its M-tiles (all N-tiles of
+// each) after its routed range, so that the shared expert's work, whose tiles
+// all read one weight matrix, is spread over the eight XCDs instead of
+// landing on the last one.  Every workgroup rebuilds the per-expert tile
+// prefix from the device offsets in LDS; the host never waits for the counts.
 //
 // Workgroup: 256 threads = 4 wavefronts, one per SIMD.  Wave w owns the
 // 32-row blocks w/2, w/2+2, .. and columns 128*(w%2) .. +128 of the tile, as
@@ -59,7 +63,15 @@
 // even) just before its MFMAs.  The k-values a lane group feeds to one MFMA
 // are then 16g + 8ks + 0..7 rather than 8(2ks + g) + 0..7; the activation
 // fragments follow the same assignment, so every MFMA still pairs equal k.
-// A step's tile is 16 KiB of activations and 8 KiB of codes.
+// A step's tile is 16 KiB of activations and 8 KiB of codes.  The
+// dequantization (16 VALU instructions per column tile) is issued in between
+// the MFMAs of its group, a quarter after each MFMA: a wavefront issues in
+// order, so a run of VALU instructions after a group of MFMAs left the matrix
+// core idle once the group's last MFMA had finished (routed up + down of the
+// V3-shaped prefill with fp8 weights: 14.7 ms with the VALU after each group,
+// 13.8 ms interleaved, 13.2 ms interleaved and with the barrier one group
+// earlier; the same schedule for the bf16 path's memory instructions was 8%
+// slower).
 #include <atomic>
 
 #include "grouped_sched.h"
@@ -321,10 +333,29 @@ __device__ __forceinline__ void fetch_rows(const GroupedGemmArgs& a, TileTab& tt
                                    (lds_void*)(&tt.ri[b][wv * 64]), 4, 0, 0);
 }
 
+// This workgroup's share of its XCD's tile list.  The list holds a range of
+// the tiles of the expert groups (expert-major, then N-tile, then M-tile:
+// rcnt tiles from global tile rlo on), followed, when the shared expert is
+// folded in as the last group, by this XCD's eighth of that group's M-tiles
+// (scnt tiles from M-tile smlo on, M-tile-major: the XCD's rows meet all
+// N-tiles while they are in L2).  Workgroup `slot` of the XCD takes list
+// entries slot, slot + nslot, ...
 struct Sched {
-  int n_groups, ntn, CN, lo, nslot, ntile;
-  __device__ __forceinline__ int tile_id(int i) const { return lo + i * nslot; }
+  int n_groups, ntn, CN, nslot, slot, ntile;
+  int rlo, rcnt, smlo, scnt;
 };
+
+__device__ __forceinline__ Tile sched_tile(const TileTab& tt, const Sched& sc, int i) {
+  const int j = sc.slot + i * sc.nslot;
+  if (j < sc.rcnt) return decode_tile(tt, sc.n_groups, sc.ntn, sc.CN, sc.rlo + j);
+  const int q = j - sc.rcnt, g = sc.n_groups - 1;
+  Tile t;
+  t.g = g;
+  t.row0 = (int64_t)tt.off[g] + (int64_t)(sc.smlo + q / sc.ntn) * BM;
+  t.rend = tt.off[g + 1];
+  t.n0 = (q % sc.ntn) * sc.CN;
+  return t;
+}
 
 // Advances the issuer past the step it has just loaded; on entering a new
 // tile, rebuilds the sources (from row indices fetched a tile earlier) and
@@ -340,11 +371,11 @@ __device__ __forceinline__ void advance(Issuer<BK, SWIGLU, W8>& is, const Groupe
   }
   ++is.it;
   is.kt = 0;
-  const Tile t = decode_tile(tt, sc.n_groups, sc.ntn, sc.CN, sc.tile_id(is.it));
+  const Tile t = sched_tile(tt, sc, is.it);
   is.build(a, tt, t, wv, lane);
   if (a.row_index && is.it + 1 < sc.ntile)
     fetch_rows(a, tt, (is.it + 1) & 1,
-               decode_tile(tt, sc.n_groups, sc.ntn, sc.CN, sc.tile_id(is.it + 1)), wv, lane);
+               sched_tile(tt, sc, is.it + 1), wv, lane);
 }
 
 // Stores the finished tile: SwiGLU (up) or plain (down), bf16, 16 bytes per
@@ -430,7 +461,10 @@ __device__ __forceinline__ void run_tile(int& g, int nk, Issuer<BK, SWIGLU, W8>&
   constexpr int KS = G::KS, LOADS = G::LOADS;
   // row groups of four MFMAs before the barrier of a step, and the loads
   // issued after each
-  constexpr int BARI = 2;  // row group of the last k-step before which B(g+1) sits
+  // row group of the last k-step before which B(g+1) sits: fp8 weights one
+  // group earlier, so that the next step's codes, read right after it, have
+  // landed before the two groups that dequantize them
+  constexpr int BARI = W8 ? 1 : 2;
   constexpr int GROUPS = 4 * (KS - 1) + BARI;
   for (int kt = 0; kt < nk; ++kt, ++g) {
     const char* cur = st[g % NS];
@@ -463,7 +497,31 @@ __device__ __forceinline__ void run_tile(int& g, int nk, Issuer<BK, SWIGLU, W8>&
           }
           __builtin_amdgcn_sched_barrier(0);
         }
-        mfma_row(i, fc, acc);
+        if constexpr (W8) {
+          // the group's dequantization (16 or 32 VALU instructions) issued
+          // between its four MFMAs, a quarter after each.  Last k-step: the
+          // next step's four column tiles over the groups after the barrier
+          // (two groups: 2 + 2; three: 2 + 1 + 1)
+          const int pos = i - BARI - 1;
+          const int ft = BARI == 1 ? 2 * pos : (pos == 0 ? 0 : pos + 1);
+          const int ntiles = s == 0 ? 1 : (pos < 0 ? 0 : (BARI == 1 || pos == 0 ? 2 : 1));
+          mfma_row(i, fc, acc);
+          if (s == 0) {
+            dequant_tile<SWIGLU>(raw, i, 1, ss, fn);
+          } else {
+#pragma unroll
+            for (int q = 0; q < 2; ++q)
+              if (q < ntiles) dequant_tile<SWIGLU>(raw, ft + q, 0, ss_next, fn);
+          }
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            if (ntiles == 1) __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
+            if (ntiles == 2) __builtin_amdgcn_sched_group_barrier(0x002, 8, 0);
+          }
+        } else {
+          mfma_row(i, fc, acc);
+        }
         __builtin_amdgcn_sched_barrier(0);
         if (grp < GROUPS) {
           // spread the LOADS loads of step g+NS-1 over the groups before B(g+1)
@@ -474,14 +532,7 @@ __device__ __forceinline__ void run_tile(int& g, int nk, Issuer<BK, SWIGLU, W8>&
           if (grp == GROUPS - 1) advance<BK, SWIGLU, W8>(is, a, tt, sc, nk, wv, lane);
         }
         if constexpr (W8) {
-          // one column tile's dequantization per group of four MFMAs
-          if (s == 0) {
-            if (i == 0) read_a<BK, SWIGLU, true>(cur, 1, wm, lane, fn);
-            dequant_tile<SWIGLU>(raw, i, 1, ss, fn);
-          } else if (i >= 2) {
-            dequant_tile<SWIGLU>(raw, 2 * (i - 2), 0, ss_next, fn);
-            dequant_tile<SWIGLU>(raw, 2 * (i - 2) + 1, 0, ss_next, fn);
-          }
+          if (s == 0 && i == 0) read_a<BK, SWIGLU, true>(cur, 1, wm, lane, fn);
         } else if (i == 0 && s < KS - 1) {
           read_frags<BK, SWIGLU>(cur, s + 1, wm, wn, lane, fn);
         }
@@ -514,18 +565,28 @@ __global__ __launch_bounds__(NTHR, 1) void gemm_bf16_persist_kernel(GroupedGemmA
   sc.n_groups = args.n_groups;
   sc.CN = CN;
   sc.ntn = (args.Nout + CN - 1) / CN;
-  const int total = total_m * sc.ntn;
   sc.nslot = gridDim.x / kNumXcd;
-  const int xcd = blockIdx.x % kNumXcd, slot = blockIdx.x / kNumXcd;
-  const int per = (total + kNumXcd - 1) / kNumXcd;
-  const int lo = xcd * per, hi = min(lo + per, total);
-  sc.lo = lo + slot;
-  if (sc.lo >= hi) return;
-  sc.ntile = (hi - sc.lo + sc.nslot - 1) / sc.nslot;
+  const int xcd = blockIdx.x % kNumXcd;
+  sc.slot = blockIdx.x / kNumXcd;
+  // A folded shared expert (the last group, B0x set) is spread over the
+  // XCDs by M-tiles; otherwise every group's tiles are cut into one range
+  // per XCD.
+  const bool fold = args.B0x != nullptr;
+  const int ms = fold ? tt.ts[sc.n_groups] - tt.ts[sc.n_groups - 1] : 0;
+  const int routed = (total_m - ms) * sc.ntn;
+  const int rper = (routed + kNumXcd - 1) / kNumXcd;
+  sc.rlo = xcd * rper;
+  sc.rcnt = max(0, min(rper, routed - sc.rlo));
+  const int msper = (ms + kNumXcd - 1) / kNumXcd;
+  sc.smlo = xcd * msper;
+  sc.scnt = max(0, min(msper, ms - sc.smlo)) * sc.ntn;
+  const int cnt = sc.rcnt + sc.scnt;
+  if (sc.slot >= cnt) return;
+  sc.ntile = (cnt - sc.slot + sc.nslot - 1) / sc.nslot;
   const int nk = args.K / BK;
 
   // tile 0's row indices, then the sources of its first steps
-  Tile t = decode_tile(tt, sc.n_groups, sc.ntn, CN, sc.tile_id(0));
+  Tile t = sched_tile(tt, sc, 0);
   if (args.row_index) {
     fetch_rows(args, tt, 0, t, wv, lane);
     wait_vm_lgkm<0>();
@@ -536,7 +597,7 @@ __global__ __launch_bounds__(NTHR, 1) void gemm_bf16_persist_kernel(GroupedGemmA
   is.kt = 0;
   is.build(args, tt, t, wv, lane);
   if (args.row_index && sc.ntile > 1)
-    fetch_rows(args, tt, 1, decode_tile(tt, sc.n_groups, sc.ntn, CN, sc.tile_id(1)), wv, lane);
+    fetch_rows(args, tt, 1, sched_tile(tt, sc, 1), wv, lane);
   // steps 0 .. NS-2 into stages 0 .. NS-2
 #pragma unroll
   for (int s = 0; s < NS - 1; ++s) {
@@ -572,12 +633,12 @@ __global__ __launch_bounds__(NTHR, 1) void gemm_bf16_persist_kernel(GroupedGemmA
   int g = 0;
   for (int i = 0; i < sc.ntile; ++i) {
     if (i > 0) {
-      t = decode_tile(tt, sc.n_groups, sc.ntn, CN, sc.tile_id(i));
+      t = sched_tile(tt, sc, i);
       if constexpr (W8) tsc = tsn;
     }
     if constexpr (W8)
       tsn = i + 1 < sc.ntile
-                ? tile_scale<SWIGLU>(args, decode_tile(tt, sc.n_groups, sc.ntn, CN, sc.tile_id(i + 1)), wn)
+                ? tile_scale<SWIGLU>(args, sched_tile(tt, sc, i + 1), wn)
                 : tsc;
 #pragma unroll
     for (int r = 0; r < MB; ++r)

@@ -24,3 +24,15 @@ def gpu_available() -> bool:
 @pytest.fixture(scope="session")
 def golden_dir():
     return os.path.join(ROOT, "tests", "golden")
+
+
+def pytest_terminal_summary(terminalreporter):
+    """The full-size parity figures (one line per workload) at the end of the run."""
+    try:
+        from parity_util import REPORT
+    except Exception:
+        return
+    if REPORT:
+        terminalreporter.write_sep("-", "full-size parity against the fp64 oracle")
+        for line in REPORT:
+            terminalreporter.write_line(line)

@@ -14,9 +14,20 @@ TIE = 1e-6  # keys closer than this may legitimately select differently
 TOL = {"f32": 1e-4, "bf16": 2e-2, "fp8": 5e-2}
 
 
+# one line per full-size comparison, printed at the end of the pytest run
+# (tests/conftest.py), so that the figures show in the run's summary even
+# when passing tests' output is captured
+REPORT: list = []
+
+
 def say(*a):
     print(*a, flush=True)
     sys.stdout.flush()
+
+
+def report(line: str):
+    REPORT.append(line)
+    say(line)
 
 
 def tol_for(cfg) -> float:

@@ -12,7 +12,7 @@ import datagen
 import oracle
 from datagen.device import upload, to_torch
 from parity_util import (TIE, bf16_floor, bf16_half_ulp, check_routing, expert_cache,
-                         oracle_route, rel_err, round_bf16, sample_tokens, say, tol_for)
+                         oracle_route, rel_err, report, round_bf16, sample_tokens, say, tol_for)
 
 pytestmark = [pytest.mark.gpu, pytest.mark.filterwarnings("ignore::RuntimeWarning")]
 
@@ -454,7 +454,7 @@ def _run_forward(lib, cfg, dev_inputs, side=True, **kw):
     return out, idx.cpu().numpy(), gate.cpu().numpy(), counts.cpu().numpy()
 
 
-def _forward_parity(lib, cfg, side=True, sample=False):
+def _forward_parity(lib, cfg, side=True, sample=False, full=False):
     """The forward against the oracle: routing of every token, and the output
     of every token (or, with ``sample``, of the tokens sample_tokens picks:
     the first and last rows of 64 experts and the rows around their first
@@ -480,8 +480,15 @@ def _forward_parity(lib, cfg, side=True, sample=False):
         got = got[tokens]
     err = rel_err(got, res["out"])
     err_delta = rel_err(got - res["x64"], res["delta"])
-    say(f"   near-ties {near}, order diffs {order}, err/RMS(out) {err:.3e}, "
-        f"err/RMS(delta) {err_delta:.3e}, idle experts {int((counts == 0).sum())}")
+    line = (f"{cfg.name} T={cfg.T} d={cfg.d} I={cfg.inter} w={cfg.w_dtype}: routed {cfg.T} tokens, "
+            f"near-ties {near}, order diffs {order}; output of "
+            f"{cfg.T if tokens is None else len(tokens)} tokens: err/RMS(out) {err:.3e}, "
+            f"err/RMS(delta) {err_delta:.3e} (bar {tol_for(cfg)}), idle experts "
+            f"{int((counts == 0).sum())}")
+    if full:
+        report(line)
+    else:
+        say("   " + line)
     assert err < tol_for(cfg)
     return out
 
@@ -503,7 +510,7 @@ def test_forward_full_size(lib, name):
     sample = name in ("v2_shaped", "v3_prefill")
     say(f"[forward-full] {name} T={cfg.T} d={cfg.d} I={cfg.inter} N={cfg.n_routed} "
         f"w={cfg.w_dtype}{' (sampled tokens)' if sample else ''}")
-    _forward_parity(lib, cfg, sample=sample)
+    _forward_parity(lib, cfg, sample=sample, full=True)
     torch.cuda.empty_cache()
 
 

@@ -50,7 +50,8 @@ def test_host_code_under_asan_and_ubsan(tmp_path):
         objs = list(ex.map(compile_one, b.sources()))
     lib = str(tmp_path / "libmoe_sanitized.so")
     r = subprocess.run([cc, "-shared", f"--offload-arch={b.ARCH}", "-Xarch_host", "-fsanitize=address",
-                        "-Xarch_host", "-fsanitize=undefined", "-shared-libasan", "-o", lib, *objs],
+                        "-Xarch_host", "-fsanitize=undefined", "-shared-libasan", "-o", lib, *objs,
+                        *b.LINK_LIBS],
                        capture_output=True, text=True)
     assert r.returncode == 0, r.stderr
     env = dict(os.environ, LD_PRELOAD=rt[-1], MOE_LIBRARY=lib,
