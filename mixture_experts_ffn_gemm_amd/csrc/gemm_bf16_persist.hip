@@ -20,13 +20,14 @@
 // landing on the last one.  Every workgroup rebuilds the per-expert tile
 // prefix from the device offsets in LDS; the host never waits for the counts.
 //
-// Workgroup: 256 threads = 4 wavefronts, one per SIMD.  Wave w owns the
-// 32-row blocks w/2, w/2+2, .. and columns 128*(w%2) .. +128 of the tile, as
-// 4 x 4 tiles of v_mfma_f32_32x32x16_bf16 with the weight fragment as the
-// first operand, so each lane accumulates 4 runs of 4 consecutive output
-// columns of one row (256 fp32 accumulators in the AGPRs).  A lane pair
-// (l, l+32) trades halves with v_permlane32_swap in the epilogue and each lane
-// stores 16 bytes.
+// Workgroup: 256 threads = 4 wavefronts, one per SIMD.  With bf16 weights
+// wave w owns the 32-row blocks w/2, w/2+2, .. and columns 128*(w%2) .. +128
+// of the tile, as 4 x 4 tiles of v_mfma_f32_32x32x16_bf16; with fp8 weights
+// it owns all eight row blocks and columns 64w .. +64 (8 x 2 tiles).  The
+// weight fragment is the first MFMA operand, so each lane accumulates 4 runs
+// of 4 consecutive output columns of one row (256 fp32 accumulators in the
+// AGPRs).  A lane pair (l, l+32) trades halves with v_permlane32_swap in the
+// epilogue and each lane stores 16 bytes.
 //
 // Every tile does all of its MFMAs, also past an expert's last row (those
 // rows are not stored): tiles of equal cost keep the workgroups of an XCD in
@@ -63,15 +64,18 @@
 // even) just before its MFMAs.  The k-values a lane group feeds to one MFMA
 // are then 16g + 8ks + 0..7 rather than 8(2ks + g) + 0..7; the activation
 // fragments follow the same assignment, so every MFMA still pairs equal k.
-// A step's tile is 16 KiB of activations and 8 KiB of codes.  The
-// dequantization (16 VALU instructions per column tile) is issued in between
-// the MFMAs of its group, a quarter after each MFMA: a wavefront issues in
-// order, so a run of VALU instructions after a group of MFMAs left the matrix
-// core idle once the group's last MFMA had finished (routed up + down of the
-// V3-shaped prefill with fp8 weights: 14.7 ms with the VALU after each group,
-// 13.8 ms interleaved, 13.2 ms interleaved and with the barrier one group
-// earlier; the same schedule for the bf16 path's memory instructions was 8%
-// slower).
+// A step's tile is 16 KiB of activations and 8 KiB of codes.  Each wave
+// owns 64 columns of all 256 rows, so every code is dequantized once per
+// workgroup (64 VALU instructions per wave and step; with the bf16 layout of
+// 128 x 128 per wave two waves dequantized each column, twice the VALU work,
+// and the routed up + down GEMMs of the V3-shaped prefill took 13.22 ms
+// against 12.91 ms).  The dequantization is issued in between the MFMAs of
+// its unit, a share after each MFMA: a wavefront issues in order, so a run
+// of VALU instructions after a group of MFMAs left the matrix core idle once
+// the group's last MFMA had finished (with the bf16 layout: 14.7 ms with the
+// VALU after each group, 13.8 ms interleaved, 13.2 ms interleaved and with
+// the barrier one group earlier; the same schedule for the bf16 path's
+// memory instructions was 8% slower).
 #include <atomic>
 
 #include "grouped_sched.h"
@@ -90,7 +94,22 @@ typedef __attribute__((address_space(3))) void lds_void;
 // block scales are wave-uniform: constant-address loads become scalar loads
 typedef __attribute__((address_space(4))) const float cfloat;
 
-constexpr int BM = 256, BN = 256, NTHR = 256, NWAVE = 4, MB = 4, NT = 4;
+constexpr int BM = 256, BN = 256, NTHR = 256, NWAVE = 4;
+
+// Wave layout in the 256 x 256 tile, as MB 32-row blocks x NT 32-column
+// tiles of MFMAs per wave (256 fp32 accumulators either way).  bf16 weights:
+// wave w owns row blocks w/2, w/2+2, .. and columns 128*(w%2) .. +128.  fp8
+// weights: wave w owns all eight row blocks and columns 64w .. +64, so that
+// each weight code is dequantized by one wave instead of two (half the VALU
+// work per step, for twice the activation fragment reads).
+template <bool W8>
+struct Lay {
+  static constexpr int MB = W8 ? 8 : 4, NT = W8 ? 2 : 4;
+  // row block of the wave's i-th row of MFMAs
+  static __device__ __forceinline__ int rblk(int i, int wv) { return W8 ? i : 2 * i + (wv >> 1); }
+  // the wave's column slot: 32*NT columns from 32*NT*wcol(wv) on
+  static __device__ __forceinline__ int wcol(int wv) { return W8 ? wv : (wv & 1); }
+};
 
 template <int BK, bool W8>
 struct Geo {
@@ -119,12 +138,14 @@ struct Geo {
   static __device__ __forceinline__ int achunk(int ks, int g) { return W8 ? 2 * g + ks : 2 * ks + g; }
 };
 
-// LDS row of column tile j of wave column wn.  Up: tiles 0, 1 are W1 rows,
-// tiles 2, 3 the W3 rows of the same output columns.
-template <bool SWIGLU>
-__device__ __forceinline__ int brow(int wn, int j) {
-  if (SWIGLU) return (j < 2 ? 0 : 128) + wn * 64 + (j & 1) * 32;
-  return wn * 128 + j * 32;
+// LDS row of column tile j of the wave in column slot wc.  Up: the first
+// half of the tiles are W1 rows, the second half the W3 rows of the same
+// output columns.
+template <bool SWIGLU, bool W8>
+__device__ __forceinline__ int brow(int wc, int j) {
+  constexpr int NT = Lay<W8>::NT, H = NT / 2;
+  if (SWIGLU) return (j < H ? 0 : 128) + wc * 32 * H + (j % H) * 32;
+  return wc * 32 * NT + j * 32;
 }
 
 // s_waitcnt on the vector-memory counter (gfx9 encoding), and on every LDS
@@ -135,32 +156,36 @@ __device__ __forceinline__ void wait_vm_lgkm() {
   __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4));
 }
 
+template <bool W8>
 struct Frags {
-  bf16x8_t a[MB], b[NT];
+  bf16x8_t a[Lay<W8>::MB], b[Lay<W8>::NT];
 };
 
-template <int BK, bool SWIGLU, bool W8>
-__device__ __forceinline__ void read_a(const char* stage, int ks, int wm, int lane, Frags& f) {
+// Activation fragments of rows lo .. lo+n-1 of the wave's MFMA rows.
+template <int BK, bool W8>
+__device__ __forceinline__ void read_a(const char* stage, int ks, int wv, int lane, Frags<W8>& f,
+                                       int lo = 0, int n = Lay<W8>::MB) {
   using G = Geo<BK, W8>;
   const int l32 = lane & 31, chunk = G::achunk(ks, lane >> 5);
 #pragma unroll
-  for (int i = 0; i < MB; ++i) {
-    const int r = (2 * i + wm) * 32 + l32;
+  for (int i = 0; i < Lay<W8>::MB; ++i) {
+    if (i < lo || i >= lo + n) continue;
+    const int r = Lay<W8>::rblk(i, wv) * 32 + l32;
     f.a[i] = *(const bf16x8_t*)(stage + r * G::ROW_BYTES + (G::swz(r, chunk) << 4));
   }
 }
 
+// bf16 weight fragments of the wave's column tiles.
 template <int BK, bool SWIGLU>
-__device__ __forceinline__ void read_frags(const char* stage, int ks, int wm, int wn, int lane,
-                                           Frags& f) {
+__device__ __forceinline__ void read_b(const char* stage, int ks, int wv, int lane,
+                                       Frags<false>& f) {
   using G = Geo<BK, false>;
   const int l32 = lane & 31, chunk = G::achunk(ks, lane >> 5);
 #pragma unroll
-  for (int j = 0; j < NT; ++j) {
-    const int r = brow<SWIGLU>(wn, j) + l32;
+  for (int j = 0; j < Lay<false>::NT; ++j) {
+    const int r = brow<SWIGLU, false>(Lay<false>::wcol(wv), j) + l32;
     f.b[j] = *(const bf16x8_t*)(stage + G::A_BYTES + r * G::ROW_BYTES + (G::swz(r, chunk) << 4));
   }
-  read_a<BK, SWIGLU, false>(stage, ks, wm, lane, f);
 }
 
 // fp8 weights: the two block scales of this wave's columns in one step (W1
@@ -169,39 +194,48 @@ struct StepScale {
   float s0, s1;
 };
 
-// 8 e4m3 codes -> bf16(code * s), round to nearest even
-__device__ __forceinline__ bf16x8_t dequant8(uint32_t w0, uint32_t w1, float s) {
-  const f32x2_t a = __builtin_amdgcn_cvt_pk_f32_fp8(w0, false);
-  const f32x2_t b = __builtin_amdgcn_cvt_pk_f32_fp8(w0, true);
-  const f32x2_t c = __builtin_amdgcn_cvt_pk_f32_fp8(w1, false);
-  const f32x2_t d = __builtin_amdgcn_cvt_pk_f32_fp8(w1, true);
-  return bf16x8_t{(__bf16)(a[0] * s), (__bf16)(a[1] * s), (__bf16)(b[0] * s), (__bf16)(b[1] * s),
-                  (__bf16)(c[0] * s), (__bf16)(c[1] * s), (__bf16)(d[0] * s), (__bf16)(d[1] * s)};
+// e4m3 codes k0 .. k0+N-1 of the 8 in (w0, w1) -> bf16(code * s) into
+// d[k0 ..], round to nearest even
+template <int K0, int N>
+__device__ __forceinline__ void dequant(uint32_t w0, uint32_t w1, float s, bf16x8_t& d) {
+#pragma unroll
+  for (int p = K0 / 2; p < (K0 + N) / 2; ++p) {
+    const uint32_t w = p < 2 ? w0 : w1;
+    const f32x2_t v = (p & 1) ? __builtin_amdgcn_cvt_pk_f32_fp8(w, true)
+                              : __builtin_amdgcn_cvt_pk_f32_fp8(w, false);
+    d[2 * p] = (__bf16)(v[0] * s);
+    d[2 * p + 1] = (__bf16)(v[1] * s);
+  }
 }
 
 // fp8 weights: the lane's 16 codes of each column tile for both k-steps of a
 // step (the first 8 for k-step 0, the last 8 for k-step 1).
 template <int BK, bool SWIGLU>
-__device__ __forceinline__ void read_w8_raw(const char* stage, int wn, int lane, u32x4_t (&raw)[NT]) {
+__device__ __forceinline__ void read_w8_raw(const char* stage, int wv, int lane,
+                                            u32x4_t (&raw)[Lay<true>::NT]) {
   using G = Geo<BK, true>;
   const int l32 = lane & 31, g = lane >> 5;
 #pragma unroll
-  for (int j = 0; j < NT; ++j) {
-    const int r = brow<SWIGLU>(wn, j) + l32;
+  for (int j = 0; j < Lay<true>::NT; ++j) {
+    const int r = brow<SWIGLU, true>(Lay<true>::wcol(wv), j) + l32;
     raw[j] = *(const u32x4_t*)(stage + G::A_BYTES + r * G::B_ROW_BYTES + (G::swz8(r, g) << 4));
   }
 }
-// column tile j of k-step ks, dequantized (W3 tiles take s1 in the up projection)
-template <bool SWIGLU>
-__device__ __forceinline__ void dequant_tile(const u32x4_t (&raw)[NT], int j, int ks, StepScale sc,
-                                             Frags& f) {
-  f.b[j] = dequant8(raw[j][2 * ks], raw[j][2 * ks + 1], SWIGLU && j >= 2 ? sc.s1 : sc.s0);
+// codes K0 .. K0+N-1 of column tile j of k-step ks, dequantized (the W3
+// tiles take s1 in the up projection)
+template <bool SWIGLU, int K0 = 0, int N = 8>
+__device__ __forceinline__ void dequant_tile(const u32x4_t (&raw)[Lay<true>::NT], int j, int ks,
+                                             StepScale sc, Frags<true>& f) {
+  dequant<K0, N>(raw[j][2 * ks], raw[j][2 * ks + 1],
+                 SWIGLU && j >= Lay<true>::NT / 2 ? sc.s1 : sc.s0, f.b[j]);
 }
 
-// The four MFMAs of row block i of one k-step.
-__device__ __forceinline__ void mfma_row(int i, const Frags& f, f32x16_t (&acc)[MB][NT]) {
+// The MFMAs of the wave's row i of one k-step.
+template <bool W8>
+__device__ __forceinline__ void mfma_row(int i, const Frags<W8>& f,
+                                         f32x16_t (&acc)[Lay<W8>::MB][Lay<W8>::NT]) {
 #pragma unroll
-  for (int j = 0; j < NT; ++j)
+  for (int j = 0; j < Lay<W8>::NT; ++j)
     acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.b[j], f.a[i], acc[i][j], 0, 0, 0);
 }
 
@@ -306,9 +340,10 @@ struct TileScale {
   cfloat *p0, *p1;
 };
 template <bool SWIGLU>
-__device__ __forceinline__ TileScale tile_scale(const GroupedGemmArgs& a, const Tile& t, int wn) {
+__device__ __forceinline__ TileScale tile_scale(const GroupedGemmArgs& a, const Tile& t, int wv) {
   const int KB = a.K / 128, NBL = a.Nout / 128;
-  int nb = (t.n0 >> 7) + (SWIGLU ? 0 : wn);
+  // the down projection's wave columns 32*NT*wcol .. +32*NT lie in one block
+  int nb = (t.n0 >> 7) + (SWIGLU ? 0 : (32 * Lay<true>::NT * Lay<true>::wcol(wv)) >> 7);
   if (nb > NBL - 1) nb = NBL - 1;  // columns past Nout: computed, never stored
   nb = __builtin_amdgcn_readfirstlane(nb);
   const int g = __builtin_amdgcn_readfirstlane(t.g);
@@ -382,17 +417,19 @@ __device__ __forceinline__ void advance(Issuer<BK, SWIGLU, W8>& is, const Groupe
 // lane.  Lane l holds output row l&31 of each 32-row block and columns
 // 8*q + 4*(l>>5) + 0..3 (q = 0..3) of each 32-column tile; after the swap
 // with lane l^32, lane l holds columns 16*p + 8*(l>>5) + 0..7 (p = 0, 1).
-template <bool SWIGLU>
-__device__ __forceinline__ void store_tile(const GroupedGemmArgs& a, const Tile& t, int wm,
-                                           int wn, int lane, f32x16_t (&acc)[MB][NT]) {
-  constexpr int NJ = SWIGLU ? NT / 2 : NT;
-  constexpr int WCOLS = SWIGLU ? 64 : 128;  // output columns per wave
+template <bool SWIGLU, bool W8>
+__device__ __forceinline__ void store_tile(const GroupedGemmArgs& a, const Tile& t, int wv,
+                                           int lane,
+                                           f32x16_t (&acc)[Lay<W8>::MB][Lay<W8>::NT]) {
+  constexpr int MB = Lay<W8>::MB, NT = Lay<W8>::NT, H = NT / 2;
+  constexpr int NJ = SWIGLU ? H : NT;
+  constexpr int WCOLS = 32 * NJ;  // output columns per wave
   bf16_t* __restrict__ C = (bf16_t*)a.C;
   const int hi = lane >> 5;
   const int64_t nrows = t.rend - t.row0;
 #pragma unroll
   for (int i = 0; i < MB; ++i) {
-    const int m = (2 * i + wm) * 32 + (lane & 31);
+    const int m = Lay<W8>::rblk(i, wv) * 32 + (lane & 31);
     const bool row_ok = m < nrows;
     bf16_t* crow = C + (t.row0 + m) * a.Nout;
 #pragma unroll
@@ -400,7 +437,7 @@ __device__ __forceinline__ void store_tile(const GroupedGemmArgs& a, const Tile&
       // keep the accumulators in the AGPRs until their tile is stored (else
       // the compiler copies all of them to VGPRs at once, and spills)
       asm volatile("" : "+a"(acc[i][j]));
-      if (SWIGLU) asm volatile("" : "+a"(acc[i][j + 2]));
+      if (SWIGLU) asm volatile("" : "+a"(acc[i][j + H]));
       unsigned p[4][2];
 #pragma unroll
       for (int q = 0; q < 4; ++q)
@@ -408,8 +445,8 @@ __device__ __forceinline__ void store_tile(const GroupedGemmArgs& a, const Tile&
         for (int h = 0; h < 2; ++h) {
           float v0, v1;
           if (SWIGLU) {
-            const float g0 = acc[i][j][4 * q + 2 * h], u0 = acc[i][j + 2][4 * q + 2 * h];
-            const float g1 = acc[i][j][4 * q + 2 * h + 1], u1 = acc[i][j + 2][4 * q + 2 * h + 1];
+            const float g0 = acc[i][j][4 * q + 2 * h], u0 = acc[i][j + H][4 * q + 2 * h];
+            const float g1 = acc[i][j][4 * q + 2 * h + 1], u1 = acc[i][j + H][4 * q + 2 * h + 1];
             v0 = g0 * __builtin_amdgcn_rcpf(1.f + __expf(-g0)) * u0;
             v1 = g1 * __builtin_amdgcn_rcpf(1.f + __expf(-g1)) * u1;
           } else {
@@ -431,7 +468,7 @@ __device__ __forceinline__ void store_tile(const GroupedGemmArgs& a, const Tile&
           p[2 * pp][h] = r[0];
           p[2 * pp + 1][h] = r[1];
         }
-        const int col = t.n0 + wn * WCOLS + j * 32 + 16 * pp + 8 * hi;
+        const int col = t.n0 + Lay<W8>::wcol(wv) * WCOLS + j * 32 + 16 * pp + 8 * hi;
         if (row_ok && col < a.Nout) {
           const u32x4_t v = {p[2 * pp][0], p[2 * pp][1], p[2 * pp + 1][0], p[2 * pp + 1][1]};
           *(u32x4_t*)(crow + col) = v;
@@ -443,7 +480,20 @@ __device__ __forceinline__ void store_tile(const GroupedGemmArgs& a, const Tile&
   }
 }
 
-// The steps of one tile.  Step g of
+// The four MFMAs of unit q (0..3) of one k-step: row q of the bf16 layout,
+// rows 2q and 2q+1 of the fp8 one.
+template <bool W8>
+__device__ __forceinline__ void mfma_unit(int q, const Frags<W8>& f,
+                                          f32x16_t (&acc)[Lay<W8>::MB][Lay<W8>::NT]) {
+  if constexpr (W8) {
+    mfma_row<true>(2 * q, f, acc);
+    mfma_row<true>(2 * q + 1, f, acc);
+  } else {
+    mfma_row<false>(q, f, acc);
+  }
+}
+
+// The steps of one tile.  Each k-step is four units of four MFMAs.  Step g of
 // the sequence reads stage g % NS; during it the loads of step g+NS-1 go into
 // stage (g-1) % NS, which every wave finished reading before barrier B(g).
 // B(g+1) follows this thread's wait for its loads of step g+1 and for all its
@@ -453,19 +503,29 @@ __device__ __forceinline__ void store_tile(const GroupedGemmArgs& a, const Tile&
 template <int BK, int NS, bool SWIGLU, bool W8>
 __device__ __forceinline__ void run_tile(int& g, int nk, Issuer<BK, SWIGLU, W8>& is,
                                          const GroupedGemmArgs& a, TileTab& tt, const Sched& sc,
-                                         char (*st)[Geo<BK, W8>::STAGE_BYTES], int wm, int wn,
-                                         int wv, int lane, Frags (&f)[2], f32x16_t (&acc)[MB][NT],
+                                         char (*st)[Geo<BK, W8>::STAGE_BYTES], int wv, int lane,
+                                         Frags<W8> (&f)[2],
+                                         f32x16_t (&acc)[Lay<W8>::MB][Lay<W8>::NT],
                                          const TileScale& tsc, const TileScale& tsn, StepScale& ss,
-                                         u32x4_t (&raw)[NT]) {
+                                         u32x4_t (&raw)[Lay<true>::NT]) {
   using G = Geo<BK, W8>;
   constexpr int KS = G::KS, LOADS = G::LOADS;
-  // row groups of four MFMAs before the barrier of a step, and the loads
-  // issued after each
-  // row group of the last k-step before which B(g+1) sits: fp8 weights one
-  // group earlier, so that the next step's codes, read right after it, have
-  // landed before the two groups that dequantize them
+  // unit of the last k-step before which B(g+1) sits: fp8 weights one unit
+  // earlier, so that the next step's codes, read right after it, have landed
+  // before the two units that dequantize them.  The loads of a step are
+  // spread over the GROUPS units before it.
   constexpr int BARI = W8 ? 1 : 2;
   constexpr int GROUPS = 4 * (KS - 1) + BARI;
+  // The activation fragments of a step's second k-step are read after its
+  // first S1 units, R1 rows after each (fp8 weights: eight reads in two
+  // halves measured 3% faster than at once; bf16 weights, and splits into
+  // four, gained nothing); those of the next step's first k-step after B(g+1).
+  constexpr int MB = Lay<W8>::MB, S1 = W8 ? 2 : 1, R1 = MB / S1;
+  // fp8 weights: the next step's first k-step is dequantized in the NU units
+  // after the unit that B(g+1) precedes, TPU column tiles in each
+  constexpr int NU = 2, TPU = Lay<true>::NT / NU;
+  static_assert(BARI + NU <= 3 || !W8, "dequantization units after B(g+1)");
+  static_assert(Lay<true>::NT == 2, "first k-step: half a column tile per unit");
   for (int kt = 0; kt < nk; ++kt, ++g) {
     const char* cur = st[g % NS];
     char* dst = st[(g + NS - 1) % NS];
@@ -479,62 +539,56 @@ __device__ __forceinline__ void run_tile(int& g, int nk, Issuer<BK, SWIGLU, W8>&
     }
 #pragma unroll
     for (int s = 0; s < KS; ++s) {
-      const Frags& fc = f[s & 1];
-      Frags& fn = f[(s + 1) & 1];
+      const Frags<W8>& fc = f[s & 1];
+      Frags<W8>& fn = f[(s + 1) & 1];
 #pragma unroll
-      for (int i = 0; i < MB; ++i) {
-        const int grp = 4 * s + i;
-        if (s == KS - 1 && i == BARI) {
+      for (int q = 0; q < 4; ++q) {
+        const int grp = 4 * s + q;
+        if (s == KS - 1 && q == BARI) {
           // B(g+1), then the fragments of the next step's first k-step (fp8
-          // weights: its codes, dequantized after this and the next group)
+          // weights: its codes, dequantized after this and the next unit)
           wait_vm_lgkm<(NS - 2) * LOADS>();
           __builtin_amdgcn_s_barrier();
-          if constexpr (W8) {
-            read_w8_raw<BK, SWIGLU>(st[(g + 1) % NS], wn, lane, raw);
-            read_a<BK, SWIGLU, true>(st[(g + 1) % NS], 0, wm, lane, fn);
-          } else {
-            read_frags<BK, SWIGLU>(st[(g + 1) % NS], 0, wm, wn, lane, fn);
-          }
+          if constexpr (W8) read_w8_raw<BK, SWIGLU>(st[(g + 1) % NS], wv, lane, raw);
+          else read_b<BK, SWIGLU>(st[(g + 1) % NS], 0, wv, lane, fn);
+          read_a<BK, W8>(st[(g + 1) % NS], 0, wv, lane, fn);
           __builtin_amdgcn_sched_barrier(0);
         }
+        mfma_unit<W8>(q, fc, acc);
         if constexpr (W8) {
-          // the group's dequantization (16 or 32 VALU instructions) issued
-          // between its four MFMAs, a quarter after each.  Last k-step: the
-          // next step's four column tiles over the groups after the barrier
-          // (two groups: 2 + 2; three: 2 + 1 + 1)
-          const int pos = i - BARI - 1;
-          const int ft = BARI == 1 ? 2 * pos : (pos == 0 ? 0 : pos + 1);
-          const int ntiles = s == 0 ? 1 : (pos < 0 ? 0 : (BARI == 1 || pos == 0 ? 2 : 1));
-          mfma_row(i, fc, acc);
+          // dequantization issued between the unit's four MFMAs.  First
+          // k-step: half a column tile of the second k-step per unit (8 VALU
+          // instructions); last k-step: the next step's two column tiles of
+          // its first k-step in the last two units (16 each).
           if (s == 0) {
-            dequant_tile<SWIGLU>(raw, i, 1, ss, fn);
-          } else {
+            if (q & 1) dequant_tile<SWIGLU, 4, 4>(raw, q >> 1, 1, ss, fn);
+            else dequant_tile<SWIGLU, 0, 4>(raw, q >> 1, 1, ss, fn);
+          } else if (q >= 4 - NU) {
 #pragma unroll
-            for (int q = 0; q < 2; ++q)
-              if (q < ntiles) dequant_tile<SWIGLU>(raw, ft + q, 0, ss_next, fn);
+            for (int t = 0; t < TPU; ++t)
+              dequant_tile<SWIGLU>(raw, (q - (4 - NU)) * TPU + t, 0, ss_next, fn);
           }
 #pragma unroll
-          for (int q = 0; q < 4; ++q) {
+          for (int m = 0; m < 4; ++m) {
             __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-            if (ntiles == 1) __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
-            if (ntiles == 2) __builtin_amdgcn_sched_group_barrier(0x002, 8, 0);
+            if (s == 0) __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);
+            else if (q >= 4 - NU) __builtin_amdgcn_sched_group_barrier(0x002, 4 * TPU, 0);
           }
-        } else {
-          mfma_row(i, fc, acc);
         }
         __builtin_amdgcn_sched_barrier(0);
         if (grp < GROUPS) {
-          // spread the LOADS loads of step g+NS-1 over the groups before B(g+1)
+          // spread the LOADS loads of step g+NS-1 over the units before B(g+1)
           const int upto = (LOADS * (grp + 1)) / GROUPS;
 #pragma unroll
           for (int j = 0; j < LOADS; ++j)
             if (j >= (LOADS * grp) / GROUPS && j < upto) is.load(j, dst, wv);
           if (grp == GROUPS - 1) advance<BK, SWIGLU, W8>(is, a, tt, sc, nk, wv, lane);
         }
-        if constexpr (W8) {
-          if (s == 0 && i == 0) read_a<BK, SWIGLU, true>(cur, 1, wm, lane, fn);
-        } else if (i == 0 && s < KS - 1) {
-          read_frags<BK, SWIGLU>(cur, s + 1, wm, wn, lane, fn);
+        if (s < KS - 1 && q < S1) {
+          // fragments of the next k-step of this step, spread over S1 units
+          if constexpr (!W8)
+            if (q == 0) read_b<BK, SWIGLU>(cur, s + 1, wv, lane, fn);
+          read_a<BK, W8>(cur, s + 1, wv, lane, fn, q * R1, R1);
         }
         __builtin_amdgcn_sched_barrier(0);
       }
@@ -553,7 +607,6 @@ __global__ __launch_bounds__(NTHR, 1) void gemm_bf16_persist_kernel(GroupedGemmA
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int wm = wv >> 1, wn = wv & 1;
   constexpr int CN = SWIGLU ? BN / 2 : BN;
 
   // per-group M-tile prefix and row offsets, in LDS for the whole kernel
@@ -615,19 +668,21 @@ __global__ __launch_bounds__(NTHR, 1) void gemm_bf16_persist_kernel(GroupedGemmA
   wait_vm_lgkm<(NS - 2) * G::LOADS>();
   __builtin_amdgcn_s_barrier();  // B(0)
 
-  Frags f[2];
-  u32x4_t raw[NT];
+  constexpr int MB = Lay<W8>::MB, NT = Lay<W8>::NT;
+  Frags<W8> f[2];
+  u32x4_t raw[Lay<true>::NT];
   TileScale tsc{}, tsn{};
   StepScale ss{0.f, 0.f};
   if constexpr (W8) {
-    tsc = tile_scale<SWIGLU>(args, t, wn);
+    tsc = tile_scale<SWIGLU>(args, t, wv);
     ss = step_scale(tsc, 0);
-    read_w8_raw<BK, SWIGLU>(st[0], wn, lane, raw);
-    read_a<BK, SWIGLU, true>(st[0], 0, wm, lane, f[0]);
+    read_w8_raw<BK, SWIGLU>(st[0], wv, lane, raw);
+    read_a<BK, true>(st[0], 0, wv, lane, f[0]);
 #pragma unroll
     for (int j = 0; j < NT; ++j) dequant_tile<SWIGLU>(raw, j, 0, ss, f[0]);
   } else {
-    read_frags<BK, SWIGLU>(st[0], 0, wm, wn, lane, f[0]);
+    read_b<BK, SWIGLU>(st[0], 0, wv, lane, f[0]);
+    read_a<BK, false>(st[0], 0, wv, lane, f[0]);
   }
   f32x16_t acc[MB][NT];
   int g = 0;
@@ -638,7 +693,7 @@ __global__ __launch_bounds__(NTHR, 1) void gemm_bf16_persist_kernel(GroupedGemmA
     }
     if constexpr (W8)
       tsn = i + 1 < sc.ntile
-                ? tile_scale<SWIGLU>(args, sched_tile(tt, sc, i + 1), wn)
+                ? tile_scale<SWIGLU>(args, sched_tile(tt, sc, i + 1), wv)
                 : tsc;
 #pragma unroll
     for (int r = 0; r < MB; ++r)
@@ -646,9 +701,9 @@ __global__ __launch_bounds__(NTHR, 1) void gemm_bf16_persist_kernel(GroupedGemmA
       for (int c = 0; c < NT; ++c)
 #pragma unroll
         for (int e = 0; e < 16; ++e) acc[r][c][e] = 0.f;
-    run_tile<BK, NS, SWIGLU, W8>(g, nk, is, args, tt, sc, st, wm, wn, wv, lane, f, acc, tsc, tsn,
+    run_tile<BK, NS, SWIGLU, W8>(g, nk, is, args, tt, sc, st, wv, lane, f, acc, tsc, tsn,
                                  ss, raw);
-    store_tile<SWIGLU>(args, t, wm, wn, lane, acc);
+    store_tile<SWIGLU, W8>(args, t, wv, lane, acc);
   }
   // no load may still be writing LDS when the workgroup ends
   wait_vm_lgkm<0>();
