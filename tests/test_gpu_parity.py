@@ -514,6 +514,22 @@ def test_forward_full_size(lib, name):
     torch.cuda.empty_cache()
 
 
+# The V3-shaped prefill in the launch configuration bench.py times: one
+# stream, the shared expert folded into the routed GEMMs as one more group
+# (spread over the eight XCDs), with bf16 weights and with fp8 e4m3 weights
+# and 128 x 128 block scales (the persistent kernel's fp8 layout); sampled
+# tokens as above.
+@pytest.mark.timeout(600)
+@pytest.mark.parametrize("w", ["bf16", "fp8"])
+def test_forward_full_size_folded(lib, w):
+    over = {} if w == "bf16" else dict(w_dtype="fp8", w_block=datagen.FP8_BLOCK)
+    cfg = datagen.get_config("v3_prefill", **over)
+    say(f"[forward-full-folded] v3_prefill T={cfg.T} d={cfg.d} I={cfg.inter} w={cfg.w_dtype} "
+        "(one stream, sampled tokens)")
+    _forward_parity(lib, cfg, side=False, sample=True, full=True)
+    torch.cuda.empty_cache()
+
+
 def test_forward_fp8_prefill(lib):
     """fp8 block-scaled weights with many rows per expert (32 experts, 150 rows
     each on average, and the 600-row shared expert) run the persistent MFMA
