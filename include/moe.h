@@ -48,8 +48,24 @@ typedef enum {
   MOE_ERR_INVALID_ARG = -1, /* a null pointer, a bad size, k > allowed experts ... */
   MOE_ERR_UNSUPPORTED = -2, /* valid but not implemented (dtype mix, alignment)   */
   MOE_ERR_WORKSPACE = -3,   /* workspace missing or smaller than required         */
-  MOE_ERR_HIP = -4          /* a HIP runtime call or kernel launch failed          */
+  MOE_ERR_HIP = -4,         /* a HIP runtime call or kernel launch failed          */
+  MOE_ERR_DEVICE_CHECK = -5 /* checked build only (libmoe_checked.so, compiled with
+                               MOE_DEVICE_CHECKS=1): a kernel found an index outside
+                               its range; see "Checked build" below                */
 } moe_status;
+
+/* Checked build.  The same sources compiled with MOE_DEVICE_CHECKS=1 give
+ * libmoe_checked.so, a debugging aid.  There the kernels test the index
+ * invariants their memory accesses rely on: top-k expert ids in [0, N), the
+ * per-expert counts adding up to T*k, gathered activation rows inside the
+ * activation matrix (for moe_expert_ffn with row_index: [0, T)), group
+ * offsets non-negative and non-decreasing, combine slots inside the T*k
+ * permuted rows, selected experts in [0, N) with finite gates.  A failed test
+ * sets a bit in a device flag word (no trap) and, where the index addresses
+ * memory, is replaced by a safe one.  Every entry point then synchronises the
+ * device before it returns (so the checked build cannot be captured into a
+ * graph) and returns MOE_ERR_DEVICE_CHECK, moe_last_error() naming the
+ * failed checks.  The ordinary build compiles the checks to nothing. */
 
 typedef enum { MOE_F32 = 0, MOE_BF16 = 1, MOE_FP8_E4M3 = 2 } moe_dtype;
 

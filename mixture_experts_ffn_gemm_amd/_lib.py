@@ -15,8 +15,12 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 # the in-tree build; MOE_LIBRARY may name another build of the same sources
 # (the host-sanitizer build of the tests)
 LIB_PATH = os.environ.get("MOE_LIBRARY") or os.path.join(PKG, "libmoe.so")
+# the same sources built with MOE_DEVICE_CHECKS=1 (kernels record index-range
+# violations; every call synchronises and reports them as MOE_ERR_DEVICE_CHECK)
+LIB_CHECKED_PATH = os.path.join(PKG, "libmoe_checked.so")
 
 MOE_OK, MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_HIP = 0, -1, -2, -3, -4
+MOE_ERR_DEVICE_CHECK = -5
 DTYPES = {"f32": 0, "bf16": 1, "fp8": 2}
 GATES = {"softmax": 0, "sigmoid": 1}
 
@@ -40,10 +44,10 @@ class MoeError(RuntimeError):
         self.status = status
 
 
-def _load():
-    if not os.path.exists(LIB_PATH):
-        raise ImportError(f"{LIB_PATH} is not built; run `python mixture_experts_ffn_gemm_amd/build.py`")
-    lib = ctypes.CDLL(LIB_PATH)
+def _load(path: str = LIB_PATH):
+    if not os.path.exists(path):
+        raise ImportError(f"{path} is not built; run `python mixture_experts_ffn_gemm_amd/build.py`")
+    lib = ctypes.CDLL(path)
     P = c_void_p
     lib.moe_status_string.restype = c_char_p
     lib.moe_status_string.argtypes = [ctypes.c_int]
@@ -81,6 +85,12 @@ NOALLOC_SCRATCH_BYTES = 64 << 20
 
 
 LIB = _load()
+
+
+def load_checked():
+    """The checked library (libmoe_checked.so), loaded beside LIB with the same
+    signatures; the binding's functions use it while ``_lib.LIB`` is set to it."""
+    return _load(LIB_CHECKED_PATH)
 
 
 def status_string(status: int) -> str:

@@ -30,6 +30,28 @@ int fail(int status, const std::string& msg) {
       return fail(MOE_ERR_HIP, std::string(#expr) + ": " + hipGetErrorString(e_)); \
   } while (0)
 
+// The end of every entry point: in the checked build, wait for the device and
+// turn the kernels' recorded check failures into MOE_ERR_DEVICE_CHECK.
+int device_checks(int st) {
+#if MOE_DEVICE_CHECKS
+  if (st != MOE_OK) return st;
+  const unsigned v = read_checks_router() | read_checks_permute() | read_checks_combine() |
+                     read_checks_gemm_persist() | read_checks_gemm_fp8() | read_checks_gemm_f32();
+  if (v == 0) return MOE_OK;
+  if (v == ~0u) return fail(MOE_ERR_HIP, "device checks: synchronising or reading the flags failed");
+  std::string m = "device checks failed:";
+  if (v & kCheckExpertId) m += " top-k expert id outside [0, N);";
+  if (v & kCheckOffsets) m += " per-expert counts do not add up to T*k;";
+  if (v & kCheckRowIndex) m += " activation row outside the activation rows;";
+  if (v & kCheckGroupRows) m += " group offsets negative or decreasing;";
+  if (v & kCheckSlot) m += " combine slot outside the T*k permuted rows;";
+  if (v & kCheckSelect) m += " selected expert outside [0, N) or non-finite gate;";
+  return fail(MOE_ERR_DEVICE_CHECK, m);
+#else
+  return st;
+#endif
+}
+
 size_t act_bytes(int dt) { return dt == MOE_F32 ? 4 : 2; }
 size_t align_up(size_t v) { return (v + 255) & ~size_t(255); }
 
@@ -242,6 +264,7 @@ int run_expert_ffn(const moe_config* c, int n_experts, const int32_t* offsets, i
   up.S1x = s3x;
   up.A = x_rows;
   up.row_index = row_index;
+  up.a_rows = row_index ? c->T : max_rows;
   up.offsets = offsets;
   up.n_groups = n_experts;
   up.max_rows = max_rows;
@@ -257,6 +280,7 @@ int run_expert_ffn(const moe_config* c, int n_experts, const int32_t* offsets, i
   dn.S0x = s2x;
   dn.A = h;
   dn.row_index = nullptr;
+  dn.a_rows = max_rows;
   dn.offsets = offsets;
   dn.n_groups = n_experts;
   dn.max_rows = max_rows;
@@ -321,6 +345,7 @@ const char* moe_status_string(int status) {
     case MOE_ERR_UNSUPPORTED: return "MOE_ERR_UNSUPPORTED";
     case MOE_ERR_WORKSPACE: return "MOE_ERR_WORKSPACE";
     case MOE_ERR_HIP: return "MOE_ERR_HIP";
+    case MOE_ERR_DEVICE_CHECK: return "MOE_ERR_DEVICE_CHECK";
     default: return "MOE_UNKNOWN_STATUS";
   }
 }
@@ -344,7 +369,8 @@ int moe_router(const moe_config* cfg, const void* x, const float* W_r, const flo
   if (!x || !W_r || !topk_idx || !topk_gate)
     return fail(MOE_ERR_INVALID_ARG, "x, W_r, topk_idx and topk_gate must be non-NULL");
   if ((st = check_ws(cfg, ws, ws_bytes))) return st;
-  return run_router(cfg, x, W_r, b, topk_idx, topk_gate, scores, ws, (hipStream_t)stream);
+  return device_checks(
+      run_router(cfg, x, W_r, b, topk_idx, topk_gate, scores, ws, (hipStream_t)stream));
 }
 
 int moe_router_masked(const moe_config* cfg, const void* x, const float* W_r, const float* b,
@@ -359,7 +385,8 @@ int moe_router_masked(const moe_config* cfg, const void* x, const float* W_r, co
   if (!x || !W_r || !topk_idx || !topk_gate)
     return fail(MOE_ERR_INVALID_ARG, "x, W_r, topk_idx and topk_gate must be non-NULL");
   if ((st = check_ws(cfg, ws, ws_bytes))) return st;
-  return run_router(cfg, x, W_r, b, topk_idx, topk_gate, scores, ws, (hipStream_t)stream, &m);
+  return device_checks(
+      run_router(cfg, x, W_r, b, topk_idx, topk_gate, scores, ws, (hipStream_t)stream, &m));
 }
 
 int moe_bias_update(const moe_config* cfg, float* b, const int32_t* counts, float gamma,
@@ -372,7 +399,7 @@ int moe_bias_update(const moe_config* cfg, float* b, const int32_t* counts, floa
     return fail(MOE_ERR_INVALID_ARG, "gamma must be finite and >= 0");
   MOE_HIP_CHECK(launch_bias_update(b, counts, cfg->n_routed, cfg->T * (int64_t)cfg->k, gamma,
                                    (hipStream_t)stream));
-  return MOE_OK;
+  return device_checks(MOE_OK);
 }
 
 int moe_permute(const moe_config* cfg, const int32_t* topk_idx, const void* x, int32_t* counts,
@@ -399,7 +426,7 @@ int moe_permute(const moe_config* cfg, const int32_t* topk_idx, const void* x, i
   if (x_perm)
     MOE_HIP_CHECK(launch_gather_rows(x, row_token, x_perm, cfg->T * cfg->k,
                                      (int64_t)cfg->d * act_bytes(cfg->act_dtype), s));
-  return MOE_OK;
+  return device_checks(MOE_OK);
 }
 
 int moe_expert_ffn(const moe_config* cfg, int32_t n_experts, const int32_t* offsets,
@@ -427,10 +454,10 @@ int moe_expert_ffn(const moe_config* cfg, int32_t n_experts, const int32_t* offs
   if (max_rows * (int64_t)inter > L.h_elems)
     return fail(MOE_ERR_WORKSPACE, "max_rows * inter exceeds the workspace sized for this config");
   if (max_rows > 0x7fffffffLL) return fail(MOE_ERR_UNSUPPORTED, "max_rows must fit int32");
-  return run_expert_ffn(cfg, n_experts, offsets, max_rows, inter, x_rows, row_index, W1, W3, W2,
-                        s1, s3, s2, at<void>(ws, L.h), y_rows, (hipStream_t)stream, nullptr, -1, -1,
-                        nullptr, nullptr, nullptr, nullptr, nullptr, nullptr,
-                        at<void>(ws, L.zrow[0]), L.zrow_elems);
+  return device_checks(run_expert_ffn(
+      cfg, n_experts, offsets, max_rows, inter, x_rows, row_index, W1, W3, W2, s1, s3, s2,
+      at<void>(ws, L.h), y_rows, (hipStream_t)stream, nullptr, -1, -1, nullptr, nullptr, nullptr,
+      nullptr, nullptr, nullptr, at<void>(ws, L.zrow[0]), L.zrow_elems));
 }
 
 int moe_combine(const moe_config* cfg, const void* y_perm, const int32_t* slot_row,
@@ -445,7 +472,7 @@ int moe_combine(const moe_config* cfg, const void* y_perm, const int32_t* slot_r
   MOE_HIP_CHECK(launch_combine(cfg->act_dtype == MOE_BF16, cfg->out_dtype == MOE_BF16, y_perm,
                                slot_row, topk_gate, y_shared, residual, out, cfg->T, cfg->d,
                                cfg->k, (hipStream_t)stream));
-  return MOE_OK;
+  return device_checks(MOE_OK);
 }
 
 static int forward_impl(const moe_config* cfg, const void* x, const float* W_r, const float* b,
@@ -562,9 +589,9 @@ int moe_forward(const moe_config* cfg, const void* x, const float* W_r, const fl
                 const float* s1s, const float* s3s, const float* s2s, void* out,
                 int32_t* topk_idx_out, float* topk_gate_out, int32_t* counts_out, void* ws,
                 size_t ws_bytes, void* stream_main, void* stream_side) {
-  return forward_impl(cfg, x, W_r, b, W1, W3, W2, s1, s3, s2, W1s, W3s, W2s, s1s, s3s, s2s, out,
-                      topk_idx_out, topk_gate_out, counts_out, ws, ws_bytes, stream_main,
-                      stream_side, nullptr);
+  return device_checks(forward_impl(cfg, x, W_r, b, W1, W3, W2, s1, s3, s2, W1s, W3s, W2s, s1s,
+                                    s3s, s2s, out, topk_idx_out, topk_gate_out, counts_out, ws,
+                                    ws_bytes, stream_main, stream_side, nullptr));
 }
 
 int moe_forward_timed(const moe_config* cfg, const void* x, const float* W_r, const float* b,
@@ -574,9 +601,9 @@ int moe_forward_timed(const moe_config* cfg, const void* x, const float* W_r, co
                       void* out, int32_t* topk_idx_out, float* topk_gate_out,
                       int32_t* counts_out, void* ws, size_t ws_bytes, void* stream_main,
                       void* stream_side, void* const* stage_events) {
-  return forward_impl(cfg, x, W_r, b, W1, W3, W2, s1, s3, s2, W1s, W3s, W2s, s1s, s3s, s2s, out,
-                      topk_idx_out, topk_gate_out, counts_out, ws, ws_bytes, stream_main,
-                      stream_side, stage_events);
+  return device_checks(forward_impl(cfg, x, W_r, b, W1, W3, W2, s1, s3, s2, W1s, W3s, W2s, s1s,
+                                    s3s, s2s, out, topk_idx_out, topk_gate_out, counts_out, ws,
+                                    ws_bytes, stream_main, stream_side, stage_events));
 }
 
 }  // extern "C"
@@ -634,7 +661,8 @@ extern "C" int moe_forward_noalloc(const moe_config* cfg, const void* x, const f
                                        " (use moe_forward with a workspace)");
   void* ws = nullptr;
   if (cfg->T > 0 && (st = scratch_for_current_device(&ws))) return st;
-  return forward_impl(cfg, x, W_r, b, W1, W3, W2, s1, s3, s2, W1s, W3s, W2s, s1s, s3s, s2s, out,
-                      topk_idx_out, topk_gate_out, counts_out, ws, MOE_NOALLOC_SCRATCH_BYTES,
-                      stream_main, stream_side, nullptr);
+  return device_checks(forward_impl(cfg, x, W_r, b, W1, W3, W2, s1, s3, s2, W1s, W3s, W2s, s1s,
+                                    s3s, s2s, out, topk_idx_out, topk_gate_out, counts_out, ws,
+                                    MOE_NOALLOC_SCRATCH_BYTES, stream_main, stream_side,
+                                    nullptr));
 }

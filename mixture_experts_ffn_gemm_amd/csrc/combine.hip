@@ -71,7 +71,9 @@ __global__ __launch_bounds__(256) void combine_kernel(const TA* __restrict__ y_p
   __shared__ int s_row[64];
   __shared__ float s_g[64];
   if (threadIdx.x < k) {
-    s_row[threadIdx.x] = slot_row[t * k + threadIdx.x];
+    int r = slot_row[t * k + threadIdx.x];
+    MOE_DCHECK_FIX(r >= 0 && r < (int64_t)gridDim.x * k, kCheckSlot, r = 0);
+    s_row[threadIdx.x] = r;
     s_g[threadIdx.x] = gate[t * k + threadIdx.x];
   }
   __syncthreads();
@@ -157,5 +159,7 @@ hipError_t launch_combine(bool act_bf16, bool out_bf16, const void* y_perm,
                                    stream);
   return hipGetLastError();
 }
+
+MOE_CHECKS_READER(combine)
 
 }  // namespace moe

@@ -300,6 +300,7 @@ struct Issuer {
           row = t.row0 + r;
           if (row > t.rend - 1) row = t.rend - 1;
         }
+        MOE_DCHECK_FIX(row >= 0 && row < a.a_rows, kCheckRowIndex, row = 0);
         const bool pad = a.zero_row && t.row0 + r >= t.rend;
         arow[j] = (pad ? (const char*)a.zero_row + (r % kZeroRows) * rowb
                        : (const char*)a.A + row * rowb) +
@@ -712,6 +713,8 @@ __global__ __launch_bounds__(NTHR, 1) void gemm_bf16_persist_kernel(GroupedGemmA
 constexpr int LIB_BK = 32, LIB_NS = 4, LIB_BK_W8 = 32, LIB_NS_W8 = 6;
 
 }  // namespace gp
+
+MOE_CHECKS_READER(gemm_persist)
 
 int persist_grid() {
   // per device: the CU count of each GPU the library runs on, read once

@@ -55,7 +55,8 @@ __global__ __launch_bounds__(256) void gemm_f32_mfma_kernel(GroupedGemmArgs args
     ld_c[i] = (q & 7) * 4;
     int64_t gr = tc.row0 + ld_r[i];
     if (gr > tc.rend - 1) gr = tc.rend - 1;
-    const int64_t src = args.row_index ? (int64_t)args.row_index[gr] : gr;
+    int64_t src = args.row_index ? (int64_t)args.row_index[gr] : gr;
+    MOE_DCHECK_FIX(src >= 0 && src < args.a_rows, kCheckRowIndex, src = 0);
     a_src[i] = A + src * K + ld_c[i];
     // Nout is a multiple of 64: every weight row of the tile exists
     const int64_t boff = ((int64_t)tc.group * Nout + tc.n0 + ld_r[i]) * K + ld_c[i];
@@ -125,6 +126,8 @@ __global__ __launch_bounds__(256) void gemm_f32_mfma_kernel(GroupedGemmArgs args
 }
 
 }  // namespace f32m
+
+MOE_CHECKS_READER(gemm_f32)
 
 hipError_t launch_gemm_f32_swiglu(const GroupedGemmArgs& a, hipStream_t s) {
   const int64_t grid = grouped_grid(a.max_rows, a.n_groups, 64, 64, a.Nout);

@@ -141,7 +141,8 @@ __device__ __forceinline__ void tile(const GroupedGemmArgs& args, const TileCoor
     for (int c = 0; c < NC; ++c) {
       int64_t r = tc.row0 + c * 16 + rl;
       if (r > tc.rend - 1) r = tc.rend - 1;
-      const int64_t src = args.row_index ? (int64_t)args.row_index[r] : r;
+      int64_t src = args.row_index ? (int64_t)args.row_index[r] : r;
+      MOE_DCHECK_FIX(src >= 0 && src < args.a_rows, kCheckRowIndex, src = 0);
       asrc[c] = (const char*)args.A + src * (int64_t)K * 2 + piece * 16;
     }
   }
@@ -281,6 +282,8 @@ __global__ __launch_bounds__(256, LB) void gemm_fp8_small_kernel(GroupedGemmArgs
 }
 
 }  // namespace f8
+
+MOE_CHECKS_READER(gemm_fp8)
 
 // Up: W1 and W3 streams, a ring of 4 k-blocks, two workgroups per CU.  Down:
 // one stream over a short K (= I), a ring of 2 k-blocks and three workgroups

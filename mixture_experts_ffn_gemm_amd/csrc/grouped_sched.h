@@ -46,6 +46,7 @@ __device__ __forceinline__ int group_tile_prefix(const int32_t* __restrict__ off
     mt[q] = 0;
     if (g < n_groups) {
       const int o0 = offsets[g], o1 = offsets[g + 1];
+      MOE_DCHECK(o0 >= 0 && o1 >= o0, kCheckGroupRows);
       mt[q] = (o1 - o0 + BM - 1) / BM;
       if (off) {
         off[g] = o0;

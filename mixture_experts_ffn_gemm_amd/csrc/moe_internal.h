@@ -5,6 +5,64 @@
 
 namespace moe {
 
+// ---------------------------------------------------------------- device checks
+// Compiled with MOE_DEVICE_CHECKS=1 (the checked library), kernels test the
+// index invariants their memory accesses rely on and record a failure as a
+// bit of their source file's flag word (an atomic OR through the vector memory
+// path; nothing traps); where the index addresses memory a safe one replaces
+// it.  Each source file's reader returns and clears its word after the device
+// has finished.  Otherwise the checks compile to nothing.
+#ifndef MOE_DEVICE_CHECKS
+#define MOE_DEVICE_CHECKS 0
+#endif
+enum : unsigned {
+  kCheckExpertId = 1u << 0,   // a top-k expert id outside [0, N) (permute clamps it)
+  kCheckOffsets = 1u << 1,    // per-expert counts not adding up to the T*k slots
+  kCheckRowIndex = 1u << 2,   // an activation row (gathered or not) outside the activation rows
+  kCheckGroupRows = 1u << 3,  // group offsets negative or decreasing
+  kCheckSlot = 1u << 4,       // a combine slot outside the T*k permuted rows
+  kCheckSelect = 1u << 5,     // a selected expert outside [0, N) or a non-finite gate
+};
+#if MOE_DEVICE_CHECKS
+static __device__ unsigned moe_check_word;
+#define MOE_DCHECK(ok, bit)                                                   \
+  do {                                                                        \
+    if (!(ok)) atomicOr(&moe_check_word, (unsigned)(bit));                    \
+  } while (0)
+// the same, and `fix` (which makes the index safe) when the test fails
+#define MOE_DCHECK_FIX(ok, bit, fix)                                          \
+  do {                                                                        \
+    if (!(ok)) {                                                              \
+      atomicOr(&moe_check_word, (unsigned)(bit));                             \
+      fix;                                                                    \
+    }                                                                         \
+  } while (0)
+#define MOE_CHECKS_READER(name)                                               \
+  unsigned read_checks_##name() {                                             \
+    unsigned v = 0;                                                           \
+    const unsigned z = 0;                                                     \
+    if (hipDeviceSynchronize() != hipSuccess ||                               \
+        hipMemcpyFromSymbol(&v, HIP_SYMBOL(moe_check_word), sizeof v) != hipSuccess || \
+        hipMemcpyToSymbol(HIP_SYMBOL(moe_check_word), &z, sizeof z) != hipSuccess)     \
+      return ~0u;                                                             \
+    return v;                                                                 \
+  }
+unsigned read_checks_router();
+unsigned read_checks_permute();
+unsigned read_checks_combine();
+unsigned read_checks_gemm_persist();
+unsigned read_checks_gemm_fp8();
+unsigned read_checks_gemm_f32();
+#else
+#define MOE_DCHECK(ok, bit) \
+  do {                      \
+  } while (0)
+#define MOE_DCHECK_FIX(ok, bit, fix) \
+  do {                               \
+  } while (0)
+#define MOE_CHECKS_READER(name)
+#endif
+
 // ---------------------------------------------------------------- helpers
 typedef uint16_t bf16_t;  // bfloat16 bit pattern
 
@@ -81,6 +139,7 @@ hipError_t launch_gather_rows(const void* x, const int32_t* row_token, void* x_p
 struct GroupedGemmArgs {
   const void* A;            // activation rows [*, K]
   const int32_t* row_index; // nullable gather map
+  int64_t a_rows;           // rows of A (the device checks' bound for gathered rows)
   const int32_t* offsets;   // [n_groups + 1] device
   int n_groups;
   int64_t max_rows;

@@ -23,7 +23,10 @@ namespace moe {
 // memory, the same way in every kernel: a bad id then routes its slot to the
 // nearest valid expert instead of indexing past the counts, the offsets or
 // the row maps.
-__device__ __forceinline__ int clamp_expert(int e, int N) { return e < 0 ? 0 : (e >= N ? N - 1 : e); }
+__device__ __forceinline__ int clamp_expert(int e, int N) {
+  MOE_DCHECK(e >= 0 && e < N, kCheckExpertId);
+  return e < 0 ? 0 : (e >= N ? N - 1 : e);
+}
 
 // Wavefront-level: counts of chunk c's experts into cnt (LDS, N entries,
 // zeroed) and each slot's rank among the equal experts of the chunk.
@@ -103,6 +106,7 @@ __global__ __launch_bounds__(256) void permute_small_kernel(
   if (tid == 0) {
     s_off[N] = tot;
     offsets[N] = tot;
+    MOE_DCHECK(tot == S, kCheckOffsets);
   }
   __syncthreads();
   for (int64_t f = tid; f < S; f += 256) {
@@ -150,6 +154,7 @@ __global__ __launch_bounds__(256) void permute_scatter_kernel(
   if (blockIdx.x == 0) {
     if (tid < N) offsets[tid] = s_off[tid];
     if (tid == 0) offsets[N] = tot;
+    if (tid == 0) MOE_DCHECK(tot == S, kCheckOffsets);
   }
   const int64_t f = (int64_t)blockIdx.x * kPermChunk + tid;
   if (f >= S) return;
@@ -235,5 +240,7 @@ hipError_t launch_gather_rows(const void* x, const int32_t* row_token, void* x_p
                                                          (u32x4_t*)x_perm, row_bytes / 16);
   return hipGetLastError();
 }
+
+MOE_CHECKS_READER(permute)
 
 }  // namespace moe

@@ -520,6 +520,7 @@ __global__ __launch_bounds__(256) void router_select_kernel(
     g_out = route_scale * my_val / tot;
   }
   if (lane < k) {
+    MOE_DCHECK(my_idx >= 0 && my_idx < N && __builtin_isfinite(g_out), kCheckSelect);
     out_idx[t * k + lane] = my_idx;
     out_gate[t * k + lane] = g_out;
   }
@@ -564,5 +565,7 @@ hipError_t launch_bias_update(float* b, const int32_t* counts, int N, int64_t sl
   bias_update_kernel<<<(unsigned)cdiv(N, 256), 256, 0, stream>>>(b, counts, N, slots, gamma);
   return hipGetLastError();
 }
+
+MOE_CHECKS_READER(router)
 
 }  // namespace moe

@@ -34,7 +34,25 @@ def test_header_symbols_exported(m):
 def test_status_strings(m):
     assert m.status_string(0) == "MOE_OK"
     assert m.status_string(-3) == "MOE_ERR_WORKSPACE"
+    assert m.status_string(-5) == "MOE_ERR_DEVICE_CHECK"
     assert "gfx950" in m.version()
+
+
+def test_checked_library_loads_and_exports(m):
+    """The checked build (MOE_DEVICE_CHECKS=1) exports the same symbols and
+    validates arguments on the host the same way."""
+    hdr = open(os.path.join(ROOT, "include", "moe.h")).read()
+    declared = set(re.findall(r"^\s*(?:const char\*|size_t|int)\s+(moe_\w+)\s*\(", hdr, re.M))
+    path = m._lib.LIB_CHECKED_PATH
+    out = subprocess.run(["nm", "-D", "--defined-only", path], capture_output=True, text=True).stdout
+    assert declared <= set(re.findall(r" T (moe_\w+)", out))
+    lib = m._lib.load_checked()
+    assert lib.moe_status_string(-5).decode() == "MOE_ERR_DEVICE_CHECK"
+    cfg = m.config_from(datagen.get_config("v3_prefill", T=64))
+    assert lib.moe_workspace_size(ctypes.byref(cfg)) == m.workspace_size(cfg)
+    bad = m.config_from(datagen.get_config("v3_prefill", T=64))
+    bad.k = 0
+    assert lib.moe_workspace_size(ctypes.byref(bad)) == 0
 
 
 def test_workspace_sizes(m):
