@@ -441,6 +441,57 @@ def test_combine(lib, act, out, k, d):
             assert np.all(np.abs(gg - want) <= bf16_half_ulp(want) + 1e-6 * m + 1e-30)
 
 
+def test_combine_against_oracle(lib):
+    """moe_combine against the oracle's combine (oracle.combine_outputs: out =
+    x + sum_j G_j E_{idx_j}(x) + y_shared).  The rows handed to the kernel are
+    the oracle's own expert outputs (oracle.swiglu per slot, in the oracle's
+    stable permutation; the shared expert's likewise) rounded to bf16; the bar
+    is what that rounding can move: sum_j |G_j| half-ulp(y_j) + half-ulp(y_sh)
+    per element, plus fp32 summation slack."""
+    cfg = datagen.get_config("v3_prefill", T=96, d=256, inter=128, n_routed=16, n_groups=1,
+                             topk_groups=1, k=6, out_dtype="f32")
+    say(f"[combine-oracle] T={cfg.T} d={cfg.d} k={cfg.k} N={cfg.n_routed}")
+    inp = datagen.MoEInputs(cfg)
+    rng = np.random.default_rng(11)
+    idx = np.stack([rng.choice(cfg.n_routed, cfg.k, replace=False)
+                    for _ in range(cfg.T)]).astype(np.int64)
+    gates = rng.uniform(0.05, 1.0, (cfg.T, cfg.k))
+    x_st = inp.x()
+    x64 = oracle.widen(x_st, cfg.act_dtype)
+    want = oracle.combine_outputs(x64, idx, gates, inp.expert, inp.shared(), cfg)
+    p = oracle.stable_permutation(idx, cfg.n_routed)
+    slot_row, row_token = p["slot_row"], p["row_token"]
+    expert_of_row = np.repeat(np.arange(cfg.n_routed), np.diff(p["offsets"]))
+    y64 = np.zeros((cfg.T * cfg.k, cfg.d))
+    for e in range(cfg.n_routed):
+        rows = np.nonzero(expert_of_row == e)[0]
+        if rows.size:
+            w1, w3, w2 = oracle.expert_weights64(cfg, inp.expert(e))
+            y64[rows] = oracle.swiglu(x64[row_token[rows]], w1, w3, w2)
+    w1, w3, w2 = oracle.expert_weights64(cfg, inp.shared())
+    ysh64 = oracle.swiglu(x64, w1, w3, w2)
+    y_perm, y_sh = round_bf16(y64), round_bf16(ysh64)
+    dev = torch.device("cuda")
+    bf = lambda a: torch.from_numpy(a.astype(np.float32)).to(torch.bfloat16).cuda()
+    got = lib.combine(lib.config_from(cfg), bf(y_perm),
+                      torch.from_numpy(slot_row.astype(np.int32)).cuda(),
+                      torch.from_numpy(gates.astype(np.float32)).cuda(),
+                      bf(y_sh),
+                      to_torch(x_st, dev))
+    torch.cuda.synchronize()
+    got = got.double().cpu().numpy()
+    g32 = gates.astype(np.float32).astype(np.float64)
+    ys = y64[slot_row.reshape(cfg.T, cfg.k)]
+    # bf16 rounding of the rows, fp32 rounding of the gates, fp32 summation
+    bound = (np.einsum("tk,tkd->td", np.abs(g32), bf16_half_ulp(ys)) + bf16_half_ulp(ysh64)
+             + np.einsum("tk,tkd->td", np.abs(g32 - gates), np.abs(ys))
+             + 1e-6 * (np.einsum("tk,tkd->td", np.abs(g32), np.abs(ys)) + np.abs(ysh64)
+                       + np.abs(x64)))
+    err = np.abs(got - want["out"])
+    assert np.all(err <= bound), float(np.max(err - bound))
+    assert rel_err(got, want["out"]) < 1e-2
+
+
 # ---------------------------------------------------------------- forward
 
 
