@@ -56,8 +56,8 @@ size_t act_bytes(int dt) { return dt == MOE_F32 ? 4 : 2; }
 size_t align_up(size_t v) { return (v + 255) & ~size_t(255); }
 
 struct Layout {
-  size_t z, idx, gate, hist, base, rank, counts, offsets, row_token, slot_row, h, y, hs, ys,
-      shoff, zrow[2], total;
+  size_t z, wplanes, idx, gate, hist, base, rank, counts, offsets, row_token, slot_row, h, y, hs,
+      ys, shoff, zrow[2], total;
   int64_t h_elems;     // capacity of the h region in activation elements
   int64_t zrow_elems;  // capacity of each zero region in bf16 elements
 };
@@ -83,6 +83,8 @@ Layout make_layout(const moe_config& c) {
   const size_t as = act_bytes(c.act_dtype);
   const int64_t nsplit = c.act_dtype == MOE_BF16 ? router_mfma_splits(T, c.d, c.n_routed) : 1;
   L.z = take(nsplit * T * N * 4);
+  // bf16 x: the three bf16 planes of W_r the MFMA router reads
+  L.wplanes = take(c.act_dtype == MOE_BF16 && router_presplit(T) ? 3 * N * d * 2 : 0);
   L.idx = take(slots * 4);
   L.gate = take(slots * 4);
   L.hist = take(nchunks * N * 4);
@@ -210,8 +212,8 @@ int run_router(const moe_config* c, const void* x, const float* W_r, const float
   int nsplit = 1;
   if (c->act_dtype == MOE_BF16) {
     nsplit = router_mfma_splits(c->T, c->d, c->n_routed);
-    MOE_HIP_CHECK(launch_router_logits_mfma((const bf16_t*)x, W_r, z, c->T, c->d, c->n_routed,
-                                            nsplit, s));
+    MOE_HIP_CHECK(launch_router_logits_mfma((const bf16_t*)x, W_r, at<bf16_t>(ws, L.wplanes), z,
+                                            c->T, c->d, c->n_routed, nsplit, s));
   } else {
     MOE_HIP_CHECK(launch_router_logits_simt(false, x, W_r, z, c->T, c->d, c->n_routed, s));
   }

@@ -96,11 +96,17 @@ __host__ __device__ inline int64_t cdiv(int64_t a, int64_t b) { return (a + b - 
 hipError_t launch_router_logits_simt(bool x_bf16, const void* x, const float* W_r, float* z,
                                      int64_t T, int d, int N, hipStream_t stream);
 
-// Router logits on MFMA for bf16 x: W_r split exactly into three bf16 parts
-// on the fly; K split into `nsplit` partial sums zpart[nsplit][T][N].
+// Router logits on MFMA for bf16 x: W_r [N, d] split exactly into three bf16
+// parts hi, mid, lo, and K split into `nsplit` partial sums
+// zpart[nsplit][T][N].  With at least kRouterPresplitBlocks blocks of 128
+// tokens the split is made once into `planes` ([3][N][d] bf16, workspace),
+// else inside each block (planes unused, may be null).
+constexpr int kRouterPresplitBlocks = 4;
+bool router_presplit(int64_t T);
 int router_mfma_splits(int64_t T, int d, int N);
-hipError_t launch_router_logits_mfma(const bf16_t* x, const float* W_r, float* zpart, int64_t T,
-                                     int d, int N, int nsplit, hipStream_t stream);
+hipError_t launch_router_logits_mfma(const bf16_t* x, const float* W_r, bf16_t* planes,
+                                     float* zpart, int64_t T, int d, int N, int nsplit,
+                                     hipStream_t stream);
 constexpr int kRouterSelectSplits = 64;  // at most this many K splits
 
 // Scores, group-limited top-k and gates from z (the sum of nsplit partials).

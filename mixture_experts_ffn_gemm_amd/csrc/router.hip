@@ -83,10 +83,11 @@ hipError_t launch_router_logits_simt(bool x_bf16, const void* x, const float* W_
 // three bf16 parts hi + mid + lo (successive round-to-nearest residuals: 8+8+8
 // significand bits cover fp32's 24), and each bf16 x bf16 product is exact in
 // the fp32 accumulator, so three v_mfma_f32_32x32x16_bf16 per fragment pair
-// give the fp32 dot product.  The split happens while the W_r tile is staged
-// into LDS.  128 tokens x 128 experts per 256-thread block, K staged 64 at a
-// time; blockIdx.z splits K (partial sums in zpart[z], added in split order by
-// the selection kernel) so that small token counts still fill the GPU.
+// give the fp32 dot product.  The split is done once per call into three bf16
+// planes of W_r's shape (router_split_kernel), not by every block that reads
+// a W_r tile.  128 tokens x 128 experts per 256-thread block, K staged 64 at
+// a time; blockIdx.z splits K (partial sums in zpart[z], added in split order
+// by the selection kernel) so that small token counts still fill the GPU.
 // ---------------------------------------------------------------------------
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
@@ -99,8 +100,32 @@ __device__ __forceinline__ uint32_t bf16_rne_bits(float f) {  // finite inputs
   return (u + 0x7fffu + ((u >> 16) & 1u)) & 0xffff0000u;
 }
 
+// planes[p * n + i] = part p of W[i] (n = N * d, a multiple of 4)
+__global__ __launch_bounds__(256) void router_split_kernel(const float* __restrict__ W,
+                                                           bf16_t* __restrict__ planes, int64_t n) {
+  const int64_t i = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4;
+  if (i >= n) return;
+  const f32x4_t w = *(const f32x4_t*)(W + i);
+  uint32_t h[4], m[4], l[4];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    h[e] = bf16_rne_bits(w[e]);
+    const float r1 = w[e] - __uint_as_float(h[e]);
+    m[e] = bf16_rne_bits(r1);
+    l[e] = bf16_rne_bits(r1 - __uint_as_float(m[e]));
+  }
+  *(u32x2_t*)(planes + i) = u32x2_t{(h[0] >> 16) | h[1], (h[2] >> 16) | h[3]};
+  *(u32x2_t*)(planes + n + i) = u32x2_t{(m[0] >> 16) | m[1], (m[2] >> 16) | m[3]};
+  *(u32x2_t*)(planes + 2 * n + i) = u32x2_t{(l[0] >> 16) | l[1], (l[2] >> 16) | l[3]};
+}
+
+// PRESPLIT: W points at the three bf16 planes; else at W_r (fp32), which each
+// block splits while it stages its tiles.  Many token blocks (prefill) share
+// every W_r tile, so the planes are made once; with one or two (decode) the
+// in-block split costs less than a pass over W_r.
+template <bool PRESPLIT>
 __global__ __launch_bounds__(256, 1) void router_logits_mfma_kernel(
-    const bf16_t* __restrict__ x, const float* __restrict__ W, float* __restrict__ zpart,
+    const bf16_t* __restrict__ x, const void* __restrict__ W, float* __restrict__ zpart,
     int64_t T, int d, int N, int nsplit) {
   constexpr int BM = 128, BN = 128, BK = 64;
   __shared__ __attribute__((aligned(16))) bf16_t lds_a[2][BM * BK];
@@ -112,6 +137,8 @@ __global__ __launch_bounds__(256, 1) void router_logits_mfma_kernel(
   const int kt0 = (int)((int64_t)blockIdx.z * nk / nsplit);
   const int kt1 = (int)((int64_t)(blockIdx.z + 1) * nk / nsplit);
 
+  // activation tile: 128 rows x 64 bf16 = 8 chunks of 16 B per row, 4 per
+  // thread, XOR-swizzled by row in LDS
   const bf16_t* a_src[4];
   int a_lds[4];
 #pragma unroll
@@ -123,50 +150,66 @@ __global__ __launch_bounds__(256, 1) void router_logits_mfma_kernel(
     a_src[i] = x + gr * d + col * 8;
     a_lds[i] = r * BK + ((col ^ (r & 7)) << 3);
   }
-  // W_r tile: 128 rows x 64 fp32 = 16 chunks of 16 B per row, 8 per thread
-  const float* b_src[8];
-  int b_lds[8];
+  // W_r tile, 128 expert rows x 64.  Planes: the activation tile's geometry,
+  // 4 chunks per thread and plane.  fp32: 16 chunks of 4 floats per row, 8 per
+  // thread, split into the planes on the way into LDS.
+  constexpr int NB = PRESPLIT ? 4 : 8;
+  const char* b_src[NB];
+  int b_lds[NB];
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
+  for (int i = 0; i < NB; ++i) {
     const int c = tid + 256 * i;
-    const int r = c >> 4, q = c & 15;  // q: 4-float group within the 64-wide K tile
+    const int r = PRESPLIT ? c >> 3 : c >> 4;
     int n = n0 + r;
     if (n > N - 1) n = N - 1;
-    b_src[i] = W + (int64_t)n * d + q * 4;
-    const int c16 = q >> 1;
-    b_lds[i] = r * BK + ((c16 ^ (r & 7)) << 3) + (q & 1) * 4;
+    if constexpr (PRESPLIT) {
+      const int col = c & 7;
+      b_src[i] = (const char*)((const bf16_t*)W + (int64_t)n * d + col * 8);
+      b_lds[i] = r * BK + ((col ^ (r & 7)) << 3);
+    } else {
+      const int q = c & 15;  // 4-float group within the 64-wide K tile
+      b_src[i] = (const char*)((const float*)W + (int64_t)n * d + q * 4);
+      b_lds[i] = r * BK + (((q >> 1) ^ (r & 7)) << 3) + (q & 1) * 4;
+    }
   }
-  u32x4_t ra[4];
-  f32x4_t rb[8];
-#define RT_GLOAD(kt_)                                                        \
-  do {                                                                       \
-    const int ko_ = (kt_) * BK;                                              \
-    _Pragma("unroll") for (int i = 0; i < 4; ++i) ra[i] =                    \
-        *(const u32x4_t*)(a_src[i] + ko_);                                   \
-    _Pragma("unroll") for (int i = 0; i < 8; ++i) rb[i] =                    \
-        *(const f32x4_t*)(b_src[i] + ko_);                                   \
-  } while (0)
-#define RT_LSTORE(buf_)                                                      \
-  do {                                                                       \
-    _Pragma("unroll") for (int i = 0; i < 4; ++i)                            \
-        *(u32x4_t*)(&lds_a[(buf_)][a_lds[i]]) = ra[i];                       \
-    _Pragma("unroll") for (int i = 0; i < 8; ++i) {                          \
-      uint32_t h[4], m[4], l[4];                                             \
-      _Pragma("unroll") for (int e = 0; e < 4; ++e) {                        \
-        const float w = rb[i][e];                                            \
-        h[e] = bf16_rne_bits(w);                                             \
-        const float r1 = w - __uint_as_float(h[e]);                          \
-        m[e] = bf16_rne_bits(r1);                                            \
-        l[e] = bf16_rne_bits(r1 - __uint_as_float(m[e]));                    \
-      }                                                                      \
-      *(u32x2_t*)(&lds_b[(buf_)][0][b_lds[i]]) =                             \
-          u32x2_t{(h[0] >> 16) | h[1], (h[2] >> 16) | h[3]};                 \
-      *(u32x2_t*)(&lds_b[(buf_)][1][b_lds[i]]) =                             \
-          u32x2_t{(m[0] >> 16) | m[1], (m[2] >> 16) | m[3]};                 \
-      *(u32x2_t*)(&lds_b[(buf_)][2][b_lds[i]]) =                             \
-          u32x2_t{(l[0] >> 16) | l[1], (l[2] >> 16) | l[3]};                 \
-    }                                                                        \
-  } while (0)
+  const int64_t pbytes = (int64_t)N * d * 2;  // bytes per plane
+  u32x4_t ra[4], rb[PRESPLIT ? 3 : 1][NB];
+  auto gload = [&](int kt) {
+    const int ko = kt * BK;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) ra[i] = *(const u32x4_t*)(a_src[i] + ko);
+#pragma unroll
+    for (int p = 0; p < (PRESPLIT ? 3 : 1); ++p)
+#pragma unroll
+      for (int i = 0; i < NB; ++i)
+        rb[p][i] = *(const u32x4_t*)(b_src[i] + p * pbytes + (int64_t)ko * (PRESPLIT ? 2 : 4));
+  };
+  auto lstore = [&](int buf) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) *(u32x4_t*)(&lds_a[buf][a_lds[i]]) = ra[i];
+    if constexpr (PRESPLIT) {
+#pragma unroll
+      for (int p = 0; p < 3; ++p)
+#pragma unroll
+        for (int i = 0; i < NB; ++i) *(u32x4_t*)(&lds_b[buf][p][b_lds[i]]) = rb[p][i];
+    } else {
+#pragma unroll
+      for (int i = 0; i < NB; ++i) {
+        uint32_t h[4], m[4], l[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float w = __uint_as_float(rb[0][i][e]);
+          h[e] = bf16_rne_bits(w);
+          const float r1 = w - __uint_as_float(h[e]);
+          m[e] = bf16_rne_bits(r1);
+          l[e] = bf16_rne_bits(r1 - __uint_as_float(m[e]));
+        }
+        *(u32x2_t*)(&lds_b[buf][0][b_lds[i]]) = u32x2_t{(h[0] >> 16) | h[1], (h[2] >> 16) | h[3]};
+        *(u32x2_t*)(&lds_b[buf][1][b_lds[i]]) = u32x2_t{(m[0] >> 16) | m[1], (m[2] >> 16) | m[3]};
+        *(u32x2_t*)(&lds_b[buf][2][b_lds[i]]) = u32x2_t{(l[0] >> 16) | l[1], (l[2] >> 16) | l[3]};
+      }
+    }
+  };
 
   const int lane = tid & 63, wv = tid >> 6;
   const int wm = wv >> 1, wn = wv & 1;
@@ -179,12 +222,12 @@ __global__ __launch_bounds__(256, 1) void router_logits_mfma_kernel(
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
-  RT_GLOAD(kt0);
-  RT_LSTORE(0);
+  gload(kt0);
+  lstore(0);
   __syncthreads();
   for (int kt = kt0; kt < kt1; ++kt) {
     const int cur = (kt - kt0) & 1;
-    if (kt + 1 < kt1) RT_GLOAD(kt + 1);
+    if (kt + 1 < kt1) gload(kt + 1);
 #pragma unroll
     for (int ks = 0; ks < BK / 16; ++ks) {
       const int chunk = 2 * ks + khalf;
@@ -209,11 +252,9 @@ __global__ __launch_bounds__(256, 1) void router_logits_mfma_kernel(
           for (int p = 0; p < 3; ++p)
             acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[p][j], acc[i][j], 0, 0, 0);
     }
-    if (kt + 1 < kt1) RT_LSTORE(cur ^ 1);
+    if (kt + 1 < kt1) lstore(cur ^ 1);
     __syncthreads();
   }
-#undef RT_GLOAD
-#undef RT_LSTORE
   float* __restrict__ zp = zpart + (int64_t)blockIdx.z * T * N;
 #pragma unroll
   for (int i = 0; i < 2; ++i)
@@ -247,10 +288,19 @@ int router_mfma_splits(int64_t T, int d, int N) {
   return (int)s;
 }
 
-hipError_t launch_router_logits_mfma(const bf16_t* x, const float* W_r, float* zpart, int64_t T,
-                                     int d, int N, int nsplit, hipStream_t stream) {
+bool router_presplit(int64_t T) { return cdiv(T, 128) >= kRouterPresplitBlocks; }
+
+hipError_t launch_router_logits_mfma(const bf16_t* x, const float* W_r, bf16_t* planes,
+                                     float* zpart, int64_t T, int d, int N, int nsplit,
+                                     hipStream_t stream) {
   dim3 grid((unsigned)cdiv(T, 128), (unsigned)cdiv(N, 128), (unsigned)nsplit);
-  router_logits_mfma_kernel<<<grid, 256, 0, stream>>>(x, W_r, zpart, T, d, N, nsplit);
+  if (router_presplit(T)) {
+    router_split_kernel<<<(unsigned)cdiv((int64_t)N * d / 4, 256), 256, 0, stream>>>(
+        W_r, planes, (int64_t)N * d);
+    router_logits_mfma_kernel<true><<<grid, 256, 0, stream>>>(x, planes, zpart, T, d, N, nsplit);
+  } else {
+    router_logits_mfma_kernel<false><<<grid, 256, 0, stream>>>(x, W_r, zpart, T, d, N, nsplit);
+  }
   return hipGetLastError();
 }
 
