@@ -200,9 +200,8 @@ int moe_permute(const moe_config* cfg, const int32_t* topk_idx, const void* x,
  * offsets = {0, T}, inter = n_shared * inter of the layer (cfg->inter is read
  * from `inter_override` when it is > 0).
  * Experts with no rows are never read.  fp8 weights, per projection: with at
- * least 128 rows per expert on average (max_rows >= 128 * n_experts) and a
- * contraction length of at least 256 (d for the up projection, inter for the
- * down projection) the codes are dequantized to bf16(code * scale) for bf16
+ * least 128 rows per expert on average (max_rows >= 128 * n_experts) the
+ * codes are dequantized to bf16(code * scale) for bf16
  * MFMAs (prefill); otherwise each expert's weights are streamed once, the
  * codes multiplied exactly and each 128-wide block's fp32 partial sum scaled
  * once (decode).  The two ways round differently (the first rounds every

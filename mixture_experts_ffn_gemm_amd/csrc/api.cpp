@@ -296,8 +296,8 @@ int run_expert_ffn(const moe_config* c, int n_experts, const int32_t* offsets, i
   // bf16: the persistent MFMA kernel (K is a multiple of 128, so at least
   // the four 32-deep steps its pipeline has stages for).  fp8: many rows per
   // expert (prefill) take the same kernel with the weights dequantized to
-  // bf16 in registers, when K covers its six stages (K >= 256); a few rows
-  // per expert (decode), or K = 128, the weight-streaming kernel, which
+  // bf16 in registers (its four stages need K >= 128, which every fp8 config
+  // has); a few rows per expert (decode), the weight-streaming kernel, which
   // takes any row count.
   auto persistent = [&](const GroupedGemmArgs& a) {
     if (c->w_dtype == MOE_BF16) return true;

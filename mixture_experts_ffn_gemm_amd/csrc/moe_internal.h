@@ -171,7 +171,7 @@ constexpr int kZeroRows = 16;
 // hipErrorInvalidValue for a smaller K.  bf16: K >= 128 (4 stages).
 hipError_t launch_gemm_bf16_persist(const GroupedGemmArgs& a, bool swiglu, hipStream_t s);
 // the same with fp8 block-scaled weights, dequantized to bf16 in registers
-// (K and Nout multiples of 128; 6 stages: K >= 192, so K >= 256)
+// (K and Nout multiples of 128; 4 stages: K >= 128)
 hipError_t launch_gemm_fp8_persist(const GroupedGemmArgs& a, bool swiglu, hipStream_t s);
 // the smallest K each persistent kernel accepts
 int persist_min_k(bool fp8_weights);

@@ -238,9 +238,9 @@ def test_expert_ffn_ragged_groups(lib, wdt):
     rows per expert on average: the weight-streaming kernel).  fp8_prefill:
     more rows per expert, the persistent MFMA kernel, whose weights are
     dequantized to bf16(code * scale); its bound models that rounding.
-    fp8_prefill_d128: the same rows with d = 128, a contraction too short for
-    that kernel's six stages: the up projection (K = d) streams its weights,
-    the down projection (K = I = 384) stays persistent.
+    fp8_prefill_d128: the same rows with d = 128, the smallest contraction the
+    persistent fp8 kernel takes (four 32-deep steps per tile, as many as its
+    pipeline has stages) for the up projection (K = d); down K = I = 384.
     bf16_small_k: K = 128 for both projections, the smallest K the bf16 path
     takes (four 32-deep steps per tile, as many as the pipeline has stages).
     bf16_many_tiles: more tiles than workgroups, so every persistent workgroup
@@ -284,10 +284,8 @@ def test_expert_ffn_ragged_groups(lib, wdt):
         if cfg.act_dtype == "bf16":
             # the same contraction with h stored as bf16, as the kernels store
             # it (and the dequantized weights rounded to bf16 where they are)
-            if wdt == "fp8_prefill":
+            if wdt in ("fp8_prefill", "fp8_prefill_d128"):
                 wk = tuple(round_bf16(wi) for wi in w)
-            elif wdt == "fp8_prefill_d128":  # only the persistent down projection rounds
-                wk = (w[0], w[1], round_bf16(w[2]))
             else:
                 wk = w
             g, u = xs @ wk[0].T, xs @ wk[1].T
