@@ -35,10 +35,12 @@ int fail(int status, const std::string& msg) {
 int device_checks(int st) {
 #if MOE_DEVICE_CHECKS
   if (st != MOE_OK) return st;
+  if (hipDeviceSynchronize() != hipSuccess)
+    return fail(MOE_ERR_HIP, "device checks: synchronising the device failed");
   const unsigned v = read_checks_router() | read_checks_permute() | read_checks_combine() |
                      read_checks_gemm_persist() | read_checks_gemm_fp8() | read_checks_gemm_f32();
   if (v == 0) return MOE_OK;
-  if (v == ~0u) return fail(MOE_ERR_HIP, "device checks: synchronising or reading the flags failed");
+  if (v == ~0u) return fail(MOE_ERR_HIP, "device checks: reading the flags failed");
   std::string m = "device checks failed:";
   if (v & kCheckExpertId) m += " top-k expert id outside [0, N);";
   if (v & kCheckOffsets) m += " per-expert counts do not add up to T*k;";

@@ -37,12 +37,12 @@ static __device__ unsigned moe_check_word;
       fix;                                                                    \
     }                                                                         \
   } while (0)
+// the file's flag word, cleared after reading (the device must be idle)
 #define MOE_CHECKS_READER(name)                                               \
   unsigned read_checks_##name() {                                             \
     unsigned v = 0;                                                           \
     const unsigned z = 0;                                                     \
-    if (hipDeviceSynchronize() != hipSuccess ||                               \
-        hipMemcpyFromSymbol(&v, HIP_SYMBOL(moe_check_word), sizeof v) != hipSuccess || \
+    if (hipMemcpyFromSymbol(&v, HIP_SYMBOL(moe_check_word), sizeof v) != hipSuccess || \
         hipMemcpyToSymbol(HIP_SYMBOL(moe_check_word), &z, sizeof z) != hipSuccess)     \
       return ~0u;                                                             \
     return v;                                                                 \

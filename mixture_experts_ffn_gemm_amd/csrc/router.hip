@@ -100,12 +100,9 @@ __device__ __forceinline__ uint32_t bf16_rne_bits(float f) {  // finite inputs
   return (u + 0x7fffu + ((u >> 16) & 1u)) & 0xffff0000u;
 }
 
-// planes[p * n + i] = part p of W[i] (n = N * d, a multiple of 4)
-__global__ __launch_bounds__(256) void router_split_kernel(const float* __restrict__ W,
-                                                           bf16_t* __restrict__ planes, int64_t n) {
-  const int64_t i = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4;
-  if (i >= n) return;
-  const f32x4_t w = *(const f32x4_t*)(W + i);
+// The three bf16 parts (hi, mid, lo) of four fp32 weights, four packed bf16
+// per part.
+__device__ __forceinline__ void split3(const f32x4_t& w, u32x2_t (&part)[3]) {
   uint32_t h[4], m[4], l[4];
 #pragma unroll
   for (int e = 0; e < 4; ++e) {
@@ -114,9 +111,20 @@ __global__ __launch_bounds__(256) void router_split_kernel(const float* __restri
     m[e] = bf16_rne_bits(r1);
     l[e] = bf16_rne_bits(r1 - __uint_as_float(m[e]));
   }
-  *(u32x2_t*)(planes + i) = u32x2_t{(h[0] >> 16) | h[1], (h[2] >> 16) | h[3]};
-  *(u32x2_t*)(planes + n + i) = u32x2_t{(m[0] >> 16) | m[1], (m[2] >> 16) | m[3]};
-  *(u32x2_t*)(planes + 2 * n + i) = u32x2_t{(l[0] >> 16) | l[1], (l[2] >> 16) | l[3]};
+  part[0] = u32x2_t{(h[0] >> 16) | h[1], (h[2] >> 16) | h[3]};
+  part[1] = u32x2_t{(m[0] >> 16) | m[1], (m[2] >> 16) | m[3]};
+  part[2] = u32x2_t{(l[0] >> 16) | l[1], (l[2] >> 16) | l[3]};
+}
+
+// planes[p * n + i] = part p of W[i] (n = N * d, a multiple of 4)
+__global__ __launch_bounds__(256) void router_split_kernel(const float* __restrict__ W,
+                                                           bf16_t* __restrict__ planes, int64_t n) {
+  const int64_t i = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4;
+  if (i >= n) return;
+  u32x2_t part[3];
+  split3(*(const f32x4_t*)(W + i), part);
+#pragma unroll
+  for (int p = 0; p < 3; ++p) *(u32x2_t*)(planes + p * n + i) = part[p];
 }
 
 // PRESPLIT: W points at the three bf16 planes; else at W_r (fp32), which each
@@ -195,18 +203,10 @@ __global__ __launch_bounds__(256, 1) void router_logits_mfma_kernel(
     } else {
 #pragma unroll
       for (int i = 0; i < NB; ++i) {
-        uint32_t h[4], m[4], l[4];
+        u32x2_t part[3];
+        split3(__builtin_bit_cast(f32x4_t, rb[0][i]), part);
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const float w = __uint_as_float(rb[0][i][e]);
-          h[e] = bf16_rne_bits(w);
-          const float r1 = w - __uint_as_float(h[e]);
-          m[e] = bf16_rne_bits(r1);
-          l[e] = bf16_rne_bits(r1 - __uint_as_float(m[e]));
-        }
-        *(u32x2_t*)(&lds_b[buf][0][b_lds[i]]) = u32x2_t{(h[0] >> 16) | h[1], (h[2] >> 16) | h[3]};
-        *(u32x2_t*)(&lds_b[buf][1][b_lds[i]]) = u32x2_t{(m[0] >> 16) | m[1], (m[2] >> 16) | m[3]};
-        *(u32x2_t*)(&lds_b[buf][2][b_lds[i]]) = u32x2_t{(l[0] >> 16) | l[1], (l[2] >> 16) | l[3]};
+        for (int p = 0; p < 3; ++p) *(u32x2_t*)(&lds_b[buf][p][b_lds[i]]) = part[p];
       }
     }
   };
