@@ -595,8 +595,9 @@ def summarize_util(csv_path, command, out_path):
     n_xcd, simds = 8, 256 * 4
     targets = {"bf16 up (prefill)": "gemm_bf16_persist_kernel<32, 4, true, false>",
                "bf16 down (prefill)": "gemm_bf16_persist_kernel<32, 4, false, false>",
-               "fp8-weight up (prefill)": "gemm_bf16_persist_kernel<32, 6, true, true>",
-               "fp8-weight down (prefill)": "gemm_bf16_persist_kernel<32, 6, false, true>",
+               # fp8 weights: any stage count (the second template argument)
+               "fp8-weight up (prefill)": ", true, true>",
+               "fp8-weight down (prefill)": ", false, true>",
                "fp8 up (decode)": "gemm_fp8_small_kernel<true, 4, 2>",
                "fp8 down (decode)": "gemm_fp8_small_kernel<false, 2, 3>"}
     lines = ["# MFMA utilisation of the main GEMM launches (rocprofv3 --pmc, one run)",
