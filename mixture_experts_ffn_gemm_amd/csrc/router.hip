@@ -130,12 +130,20 @@ __global__ __launch_bounds__(256) void router_split_kernel(const float* __restri
 // PRESPLIT: W points at the three bf16 planes; else at W_r (fp32), which each
 // block splits while it stages its tiles.  Many token blocks (prefill) share
 // every W_r tile, so the planes are made once; with one or two (decode) the
-// in-block split costs less than a pass over W_r.
+// in-block split costs less than a pass over W_r.  With the planes, K is
+// staged 32 at a time (64 KiB of LDS, two blocks per CU, so one block's
+// loads and barrier overlap the other's MFMAs); the in-block split stages 64.
 template <bool PRESPLIT>
-__global__ __launch_bounds__(256, 1) void router_logits_mfma_kernel(
+__global__ __launch_bounds__(256, PRESPLIT ? 2 : 1) void router_logits_mfma_kernel(
     const bf16_t* __restrict__ x, const void* __restrict__ W, float* __restrict__ zpart,
     int64_t T, int d, int N, int nsplit) {
-  constexpr int BM = 128, BN = 128, BK = 64;
+  constexpr int BM = 128, BN = 128, BK = PRESPLIT ? 32 : 64;
+  constexpr int CPR = BK / 8;           // 16-byte chunks per LDS row
+  constexpr int AC = BM * CPR / 256;    // activation chunks per thread
+  // chunk c of row r sits at chunk swz(r, c): the 16 rows a quarter-wave reads
+  // with one ds_read_b128 fall on distinct banks (64-byte rows: 4 rows per
+  // 256 bytes, so rows 4 apart are told apart; 128-byte rows: 2 per 256)
+  auto swz = [](int r, int c) { return PRESPLIT ? c ^ ((r >> 2) & 3) : c ^ (r & 7); };
   __shared__ __attribute__((aligned(16))) bf16_t lds_a[2][BM * BK];
   __shared__ __attribute__((aligned(16))) bf16_t lds_b[2][3][BN * BK];
   const int tid = threadIdx.x;
@@ -145,47 +153,47 @@ __global__ __launch_bounds__(256, 1) void router_logits_mfma_kernel(
   const int kt0 = (int)((int64_t)blockIdx.z * nk / nsplit);
   const int kt1 = (int)((int64_t)(blockIdx.z + 1) * nk / nsplit);
 
-  // activation tile: 128 rows x 64 bf16 = 8 chunks of 16 B per row, 4 per
-  // thread, XOR-swizzled by row in LDS
-  const bf16_t* a_src[4];
-  int a_lds[4];
+  // activation tile: 128 rows x BK bf16 = CPR chunks of 16 B per row, AC per
+  // thread, swizzled by row in LDS
+  const bf16_t* a_src[AC];
+  int a_lds[AC];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
+  for (int i = 0; i < AC; ++i) {
     const int c = tid + 256 * i;
-    const int r = c >> 3, col = c & 7;
+    const int r = c / CPR, col = c % CPR;
     int64_t gr = m0 + r;
     if (gr > T - 1) gr = T - 1;
     a_src[i] = x + gr * d + col * 8;
-    a_lds[i] = r * BK + ((col ^ (r & 7)) << 3);
+    a_lds[i] = r * BK + (swz(r, col) << 3);
   }
-  // W_r tile, 128 expert rows x 64.  Planes: the activation tile's geometry,
-  // 4 chunks per thread and plane.  fp32: 16 chunks of 4 floats per row, 8 per
-  // thread, split into the planes on the way into LDS.
-  constexpr int NB = PRESPLIT ? 4 : 8;
+  // W_r tile, 128 expert rows x BK.  Planes: the activation tile's geometry,
+  // AC chunks per thread and plane.  fp32 (BK = 64): 16 chunks of 4 floats per
+  // row, 8 per thread, split into the planes on the way into LDS.
+  constexpr int NB = PRESPLIT ? AC : 8;
   const char* b_src[NB];
   int b_lds[NB];
 #pragma unroll
   for (int i = 0; i < NB; ++i) {
     const int c = tid + 256 * i;
-    const int r = PRESPLIT ? c >> 3 : c >> 4;
+    const int r = PRESPLIT ? c / CPR : c >> 4;
     int n = n0 + r;
     if (n > N - 1) n = N - 1;
     if constexpr (PRESPLIT) {
-      const int col = c & 7;
+      const int col = c % CPR;
       b_src[i] = (const char*)((const bf16_t*)W + (int64_t)n * d + col * 8);
-      b_lds[i] = r * BK + ((col ^ (r & 7)) << 3);
+      b_lds[i] = r * BK + (swz(r, col) << 3);
     } else {
       const int q = c & 15;  // 4-float group within the 64-wide K tile
       b_src[i] = (const char*)((const float*)W + (int64_t)n * d + q * 4);
-      b_lds[i] = r * BK + (((q >> 1) ^ (r & 7)) << 3) + (q & 1) * 4;
+      b_lds[i] = r * BK + (swz(r, q >> 1) << 3) + (q & 1) * 4;
     }
   }
   const int64_t pbytes = (int64_t)N * d * 2;  // bytes per plane
-  u32x4_t ra[4], rb[PRESPLIT ? 3 : 1][NB];
+  u32x4_t ra[AC], rb[PRESPLIT ? 3 : 1][NB];
   auto gload = [&](int kt) {
     const int ko = kt * BK;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) ra[i] = *(const u32x4_t*)(a_src[i] + ko);
+    for (int i = 0; i < AC; ++i) ra[i] = *(const u32x4_t*)(a_src[i] + ko);
 #pragma unroll
     for (int p = 0; p < (PRESPLIT ? 3 : 1); ++p)
 #pragma unroll
@@ -194,7 +202,7 @@ __global__ __launch_bounds__(256, 1) void router_logits_mfma_kernel(
   };
   auto lstore = [&](int buf) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) *(u32x4_t*)(&lds_a[buf][a_lds[i]]) = ra[i];
+    for (int i = 0; i < AC; ++i) *(u32x4_t*)(&lds_a[buf][a_lds[i]]) = ra[i];
     if constexpr (PRESPLIT) {
 #pragma unroll
       for (int p = 0; p < 3; ++p)
@@ -235,14 +243,14 @@ __global__ __launch_bounds__(256, 1) void router_logits_mfma_kernel(
 #pragma unroll
       for (int i = 0; i < 2; ++i) {
         const int r = wm * 64 + i * 32 + l32;
-        af[i] = *(const bf16x8_t*)(&lds_a[cur][r * BK + ((chunk ^ (r & 7)) << 3)]);
+        af[i] = *(const bf16x8_t*)(&lds_a[cur][r * BK + (swz(r, chunk) << 3)]);
       }
 #pragma unroll
       for (int p = 0; p < 3; ++p)
 #pragma unroll
         for (int j = 0; j < 2; ++j) {
           const int r = wn * 64 + j * 32 + l32;
-          bfr[p][j] = *(const bf16x8_t*)(&lds_b[cur][p][r * BK + ((chunk ^ (r & 7)) << 3)]);
+          bfr[p][j] = *(const bf16x8_t*)(&lds_b[cur][p][r * BK + (swz(r, chunk) << 3)]);
         }
 #pragma unroll
       for (int i = 0; i < 2; ++i)
