@@ -563,19 +563,23 @@ def test_forward_full_size(lib, name):
     torch.cuda.empty_cache()
 
 
-# The V3-shaped prefill in the launch configuration bench.py times: one
-# stream, the shared expert folded into the routed GEMMs as one more group
-# (spread over the eight XCDs), with bf16 weights and with fp8 e4m3 weights
-# and 128 x 128 block scales (the persistent kernel's fp8 layout); sampled
-# tokens as above.
+# The workloads with one shared expert in the launch configuration bench.py
+# times: one stream, the shared expert folded into the routed GEMMs as one
+# more group (spread over the eight XCDs).  The V3-shaped prefill with bf16
+# weights and with fp8 e4m3 weights and 128 x 128 block scales (the
+# persistent kernel's fp8 layout), sampled tokens as above; the DeepSeekMoE
+# layer and the fp8 decode step, every token.
 @pytest.mark.timeout(600)
-@pytest.mark.parametrize("w", ["bf16", "fp8"])
-def test_forward_full_size_folded(lib, w):
-    over = {} if w == "bf16" else dict(w_dtype="fp8", w_block=datagen.FP8_BLOCK)
-    cfg = datagen.get_config("v3_prefill", **over)
-    say(f"[forward-full-folded] v3_prefill T={cfg.T} d={cfg.d} I={cfg.inter} w={cfg.w_dtype} "
-        "(one stream, sampled tokens)")
-    _forward_parity(lib, cfg, side=False, sample=True, full=True)
+@pytest.mark.parametrize("name,w", [("v3_prefill", "bf16"), ("v3_prefill", "fp8"),
+                                    ("deepseekmoe_2b", "bf16"), ("v3_decode", "fp8")])
+def test_forward_full_size_folded(lib, name, w):
+    over = dict(w_dtype="fp8", w_block=datagen.FP8_BLOCK) if w == "fp8" and name == "v3_prefill" else {}
+    cfg = datagen.get_config(name, **over)
+    assert cfg.w_dtype == w and cfg.n_shared == 1
+    sample = name == "v3_prefill"
+    say(f"[forward-full-folded] {name} T={cfg.T} d={cfg.d} I={cfg.inter} w={cfg.w_dtype} "
+        f"(one stream{', sampled tokens' if sample else ''})")
+    _forward_parity(lib, cfg, side=False, sample=sample, full=True)
     torch.cuda.empty_cache()
 
 
