@@ -2,8 +2,9 @@
 kept out of every kernel: the build passes the target feature that turns them
 off, this test shows on a control kernel that the feature does remove them
 from the gfx950 code hipcc makes, and that none occurs in the device code of
-the built library.  The device code is read from the library's own fat
-binary (clang-offload-bundler + llvm-objdump): assembly of code built here."""
+the built libraries (the ordinary and the checked one).  The device code is
+read from each library's own fat binary (clang-offload-bundler +
+llvm-objdump): assembly of code built here."""
 import os
 import re
 import shutil
@@ -54,11 +55,12 @@ def test_feature_flag_removes_packed_fp32_from_a_control_kernel():
     assert not PACKED.search(asm["with"])
 
 
-def test_built_library_has_no_packed_fp32():
+@pytest.mark.parametrize("name", ["libmoe.so", "libmoe_checked.so"])
+def test_built_library_has_no_packed_fp32(name):
     _tools()
-    lib = os.path.join(ROOT, "mixture_experts_ffn_gemm_amd", "libmoe.so")
+    lib = os.path.join(ROOT, "mixture_experts_ffn_gemm_amd", name)
     if not os.path.exists(lib):
-        pytest.skip("libmoe.so not built")
+        pytest.skip(f"{name} not built")
     with tempfile.TemporaryDirectory() as tmp:
         fat = os.path.join(tmp, "fat.bin")
         subprocess.run([os.path.join(LLVM, "llvm-objcopy"), f"--dump-section=.hip_fatbin={fat}", lib],
